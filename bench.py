@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the output-stationary tiled GEMM C = A @ B on one MI355X.
+
+A step is one gemm_run (one kernel launch) over resident device inputs; the
+default workload is the square bf16 product M = N = K = 8192 (bf16 inputs, fp32
+accumulation, bf16 output). Prints ONE JSON line on stdout:
+
+  value        TFLOP/s = 2*M*N*K / (time per step)
+  roofline     the dominant kernel against its roof: MFMA peak (dense bf16
+               2516.6 TFLOP/s = 256 CUs x 4096 flop/clk x 2.4 GHz) for
+               compute-bound shapes, HBM (8000 GB/s, compulsory bytes) otherwise;
+               `achieved` uses the kernel's average launch time from HIP events
+               on the launch stream; `traffic` = HBM bytes per launch from the
+               committed rocprofv3 counter file of this kernel source, else null
+  cpu_baseline the oracle (plain CPU triple loop, binary64 sums) timed on a
+               bounded sample of rows of the same product on the host cores
+  check        the sampled rows of the GPU result against those oracle rows
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s and % of MFMA peak at 1 GPU (bf16 8192³; ragged shapes)"
+PEAK_MFMA_16BIT_TFLOPS = 2516.6  # dense fp16/bf16: 256 CUs x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBPS = 8000.0
+RIDGE = PEAK_MFMA_16BIT_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)  # flop per byte
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "tiled_gemm_output_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, sha: str):
+    """HBM bytes per launch from profiles/counters_<workload>.json if it was taken
+    on this kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != sha:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_threads() -> int:
+    n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(o, a, b, w, target_s: float):
+    """Time the oracle on a bounded set of full rows; return (baseline dict, rows, oracle rows)."""
+    import numpy as np
+
+    threads = cpu_threads()
+    in_kind, out_kind = w.in_kind, w.out_kind
+    rng = np.random.default_rng(w.index)
+    # calibrate with one row per thread
+    probe = np.sort(rng.choice(w.M, size=min(threads, w.M), replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    o.gemm_rows(a, b, probe, in_kind, out_kind, threads=threads)
+    t_probe = time.perf_counter() - t0
+    per_round = max(t_probe, 1e-4)  # one row per thread
+    rounds = max(1, int(target_s / per_round))
+    n = int(min(w.M, rounds * len(probe)))
+    rows = np.sort(rng.choice(w.M, size=n, replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    ref = o.gemm_rows(a, b, rows, in_kind, out_kind, threads=threads)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * n * w.N * w.K
+    base = {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d of the %d output rows (%d x %d x %d x 2 = %.3g flop, binary64 sums) in %.1f s; "
+                  "full product extrapolates to %.0f s" % (n, w.M, n, w.N, w.K, flops, dt,
+                                                            2.0 * w.M * w.N * w.K / (flops / dt)),
+    }
+    return base, rows, ref
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="square8192_bf16")
+    ap.add_argument("--tile", default=None, help="force a tile, e.g. 256,256,64")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        log("bench.py: this build runs on one GPU only; --gpus %d is not supported. "
+            "The multi-GPU sharding of this product is described in DESIGN.md." % args.gpus)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from tiled_gemm_output_amd import inputs, tgemm
+
+    if not os.path.exists(tgemm.LIBRARY):
+        from tiled_gemm_output_amd import build as lib_build
+
+        lib_build.build()
+    if not torch.cuda.is_available():
+        log("bench.py: no GPU visible")
+        return 1
+    torch.cuda.set_device(0)
+    w = inputs.WORKLOADS[args.workload]
+    dtype = tgemm.DTYPES[w.dtype]
+    log("bench: workload %s M=%d N=%d K=%d dtype=%s" % (w.name, w.M, w.N, w.K, w.dtype))
+    a, b = inputs.make(w)
+    da = torch.from_numpy(a.view(np.int16 if a.dtype == np.uint16 else np.int32)).cuda()
+    db = torch.from_numpy(b.view(np.int16 if b.dtype == np.uint16 else np.int32)).cuda()
+    ob = tgemm.OUT_BYTES[dtype]
+    dc = torch.empty((w.M, w.N), dtype=torch.int16 if ob == 2 else torch.int32, device="cuda")
+    h = tgemm.gemm_create()
+    if args.tile:
+        tgemm.check(tgemm.gemm_set_tile(h, *[int(x) for x in args.tile.split(",")]))
+    plan = tgemm.gemm_plan(h, w.M, w.N, w.K, da.data_ptr(), w.K, db.data_ptr(), w.N, dc.data_ptr(), w.N, dtype)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step():
+        tgemm.check(tgemm.gemm_run(h, w.M, w.N, w.K, da.data_ptr(), w.K, db.data_ptr(), w.N, dc.data_ptr(), w.N,
+                                   dtype, sp), "gemm_run")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("bench: warmup done (%d steps), timing %d steps" % (args.warmup, args.steps))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per_launch_ms = [s.elapsed_time(e) for s, e in ev]
+    ms_per_step = total_ms / args.steps
+    launch_ms = float(np.mean(per_launch_ms))
+    flops = 2.0 * w.M * w.N * w.K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    log("bench: %.4f ms/step (events), %.4f ms/launch (mean), min %.4f, wall %.3f s" %
+        (ms_per_step, launch_ms, min(per_launch_ms), wall))
+
+    ib = 2 if dtype != tgemm.I32_I32 else 4
+    compulsory = ib * (w.M * w.K + w.K * w.N) + ob * w.M * w.N
+    intensity = flops / compulsory
+    sha = kernel_source_sha()
+    traffic = load_traffic(w.name, sha)
+    if intensity >= RIDGE:
+        achieved = flops / (launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_16BIT_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_MFMA_16BIT_TFLOPS, "traffic": traffic}
+    else:
+        achieved = compulsory / (launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic}
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.in_kind == "bf16" else w.in_kind,
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.in_kind, "acc": "fp32" if ib == 2 else "i32",
+                   "out": w.out_kind, "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
+                   "kernel": plan["kernel_name"], "grid": plan["grid"], "threads": plan["threads"],
+                   "vector_loads": plan["vector_loads"], "kernel_source_sha": sha},
+        "pct_of_mfma_peak": 100.0 * value / PEAK_MFMA_16BIT_TFLOPS,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        o = oracle.get()
+        base, rows, ref = cpu_baseline(o, a, b, w, args.cpu_seconds)
+        result["cpu_baseline"] = base
+        got = dc[torch.from_numpy(rows).cuda()].cpu().numpy()
+        if w.out_kind == "f32":
+            gv = got.view(np.float32).astype(np.float64)
+            rv = ref.astype(np.float64)
+        else:
+            gv = (got.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64) \
+                if w.out_kind == "bf16" else got.view(np.float16).astype(np.float64)
+            rv = (ref.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64) \
+                if w.out_kind == "bf16" else ref.view(np.float16).astype(np.float64)
+        scale = float(np.max(np.abs(rv)))
+        err = np.abs(gv - rv)
+        p_bits, emin = {"f32": (24, -126), "bf16": (8, -126), "f16": (11, -14)}[w.out_kind]
+        ulp = np.exp2(np.maximum(np.floor(np.log2(np.where(rv != 0, np.abs(rv), 1.0))), emin) - (p_bits - 1))
+        ok = bool(np.all(err <= np.maximum(2e-3 * scale, ulp)))
+        result["check"] = {"rows": int(len(rows)), "rule": "|C-R| <= max(2e-3*max|R|, 1 ulp of R)",
+                           "passed": ok, "max_err_over_max_abs": float(err.max() / scale),
+                           "max_err_ulps": float(np.max(err / ulp)),
+                           "differing_elements": int(np.sum(got.view(np.int16 if ob == 2 else np.int32)
+                                                            != ref.view(np.int16 if ob == 2 else np.int32)))}
+    tgemm.gemm_destroy(h)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

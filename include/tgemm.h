@@ -1,0 +1,135 @@
+/*
+ * tgemm.h -- output-stationary tiled matrix multiply C = A @ B on MI355X (gfx950).
+ *
+ * The operation ("Reading a matrix multiply through its tiles", opening paragraph
+ * and section "Keep one output tile resident"; Mojo GPU puzzles, "Tiled Matrix
+ * Multiplication", section 3, which fixes it as A x B and not A x B^T):
+ *
+ *     C[i][j] = sum_{k < K} A[i][k] * B[k][j]      0 <= i < M, 0 <= j < N
+ *
+ * A is M x K, B is K x N, C is M x N, all row-major (the puzzle page's "row-major
+ * layout for all tensors") with leading dimensions lda, ldb, ldc counted in
+ * ELEMENTS. C is overwritten: no alpha/beta, no accumulate into C (each page
+ * stores the finished accumulator tile exactly once). Each C tile's fp32 (int32
+ * for the integer path) accumulator stays in registers for the whole reduction;
+ * A and B K-tiles are staged through LDS; partial edge tiles are handled over
+ * their actual row, column and reduction ranges ("Edge tiles still matter").
+ *
+ * Number formats (dtype): the inputs A and B share one format; the accumulator is
+ * fp32 for 16-bit float inputs (Helion matmul page: the C tile is an fp32 zero
+ * tile; "What fits in local storage?": FP16 inputs with FP32 accumulation) and
+ * the result is rounded once, to nearest-even, into C's format. The integer path
+ * sums in 32-bit two's complement and wraps modulo 2^32.
+ *
+ * Conventions shared by every entry point:
+ *  - All pointers A, B, C are DEVICE pointers (memory of the current HIP device),
+ *    owned by the caller; the library never frees or retains them.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream), owned by
+ *    the caller. gemm_run only enqueues work and returns; it never synchronizes.
+ *    Faults inside a launched kernel surface at the caller's next synchronization.
+ *  - Argument errors are detected on the host BEFORE any HIP call and leave C
+ *    untouched. No C++ exception crosses this interface.
+ *  - C must not overlap A or B (not checked).
+ *  - Any alignment of A, B, C and any leading dimension >= the row length is
+ *    accepted; a slower element-wise loader is used when 16-byte vector loads are
+ *    not possible.
+ *  - A handle may be used by one host thread at a time.
+ */
+#ifndef TGEMM_H
+#define TGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tgemm_handle* gemm_handle_t;
+
+/* Status codes (int32). */
+typedef enum {
+  GEMM_OK = 0,
+  GEMM_ERR_INVALID_ARG = 1,       /* null/negative/too-small argument, destroyed or null handle */
+  GEMM_ERR_UNSUPPORTED_DTYPE = 2, /* dtype is not one of gemm_dtype_t */
+  GEMM_ERR_NO_DEVICE = 3,         /* no HIP device visible */
+  GEMM_ERR_ARCH = 4,              /* current device is not gfx950 */
+  GEMM_ERR_HIP = 5,               /* a HIP runtime call or kernel launch failed */
+  GEMM_ERR_OUT_OF_MEMORY = 6,     /* host allocation of the handle failed */
+  GEMM_ERR_UNSUPPORTED_TILE = 7   /* gemm_set_tile asked for a tile no kernel has, for this dtype */
+} gemm_status_t;
+
+/* Input/accumulator/output formats (int32). */
+typedef enum {
+  GEMM_I32_I32 = 0,   /* int32 in, int32 accumulate (wraps mod 2^32), int32 out */
+  GEMM_F16_F32 = 1,   /* IEEE binary16 in, fp32 accumulate, fp32 out */
+  GEMM_BF16_F32 = 2,  /* bfloat16 in, fp32 accumulate, fp32 out */
+  GEMM_BF16_BF16 = 3, /* bfloat16 in, fp32 accumulate, bfloat16 out (round to nearest even) */
+  GEMM_F16_F16 = 4    /* binary16 in, fp32 accumulate, binary16 out (round to nearest even) */
+} gemm_dtype_t;
+
+/* The kernel configuration gemm_run would use for a call (see gemm_plan). */
+typedef struct {
+  int32_t tile_m, tile_n, tile_k; /* C tile rows/cols and K-step of one workgroup */
+  int32_t threads;                /* threads per workgroup */
+  int32_t vector_loads;           /* 1: 16-byte loads straight into LDS; 0: element-wise loader */
+  int32_t kernel;                 /* 0 none (empty C), 1 zero fill (K = 0), 2 int32 VALU,
+                                     3 one-wave 16x16x32 MFMA, 4 macro-tile MFMA */
+  int64_t grid;                   /* workgroups launched */
+  int32_t lds_bytes;              /* LDS per workgroup */
+  int32_t reserved;
+} gemm_plan_t;
+
+/* Create a handle on the CURRENT HIP device. Host-only: no device work is enqueued.
+ * Returns GEMM_ERR_NO_DEVICE if no device is visible, GEMM_ERR_ARCH if the current
+ * device is not gfx950, GEMM_ERR_INVALID_ARG if out is NULL. On success *out owns
+ * the handle until gemm_destroy. */
+gemm_status_t gemm_create(gemm_handle_t* out);
+
+/* C = A @ B (see the top of this file). Enqueues on `stream` and returns.
+ *   M, N, K    >= 0. M == 0 or N == 0: nothing is launched. K == 0: C is filled
+ *              with zeros (the empty sum).
+ *   A          device pointer, M x K, row stride lda >= max(K, 1) elements.
+ *   B          device pointer, K x N, row stride ldb >= max(N, 1) elements.
+ *   C          device pointer, M x N, row stride ldc >= max(N, 1) elements.
+ *   A/B/C may be NULL only when the matrix has no elements.
+ *   dtype      one of gemm_dtype_t; element sizes: 4 (i32), 2 (f16, bf16) for A/B;
+ *              4 for *_F32 and I32 outputs, 2 for *_BF16 and *_F16 outputs.
+ * Errors: GEMM_ERR_INVALID_ARG, GEMM_ERR_UNSUPPORTED_DTYPE, GEMM_ERR_UNSUPPORTED_TILE
+ * (a forced tile this dtype has no kernel for), GEMM_ERR_HIP (launch failed). */
+gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, void* C, int64_t ldc, gemm_dtype_t dtype, void* stream);
+
+/* Release a handle. NULL or an already destroyed handle -> GEMM_ERR_INVALID_ARG. */
+gemm_status_t gemm_destroy(gemm_handle_t h);
+
+/* Force the C tile (tm x tn) and K-step tk of later gemm_run calls on this handle;
+ * (0, 0, 0) returns to the library's own choice. The pages' tiles are available:
+ * 3x3x3 (and any tm*tn <= 1024 with a 64 KiB LDS budget) for int32 -- the Mojo
+ * puzzle's 9x9 example; 16x16x32 for the float formats -- the traffic example of
+ * "Count the repeated reads"; 64x64x64 -- "Edge tiles still matter". Float formats
+ * also offer 128x128x64, 256x128x64 and 256x256x64. Whether a tile fits the dtype
+ * is checked by gemm_run/gemm_plan (GEMM_ERR_UNSUPPORTED_TILE). Negative values or
+ * a partial zero triple -> GEMM_ERR_INVALID_ARG. */
+gemm_status_t gemm_set_tile(gemm_handle_t h, int32_t tm, int32_t tn, int32_t tk);
+
+/* Validate gemm_run's arguments without a handle and without any HIP call.
+ * Returns exactly the status gemm_run would return for an argument error, or
+ * GEMM_OK. */
+gemm_status_t gemm_check_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                              int64_t ldb, const void* C, int64_t ldc, gemm_dtype_t dtype);
+
+/* The configuration gemm_run would use for these arguments on this handle
+ * (honouring gemm_set_tile). Host-only. h may be NULL (then the automatic
+ * choice is reported). Errors as gemm_check_args, plus GEMM_ERR_UNSUPPORTED_TILE. */
+gemm_status_t gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                        const void* B, int64_t ldb, const void* C, int64_t ldc, gemm_dtype_t dtype,
+                        gemm_plan_t* out);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* gemm_status_string(gemm_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGEMM_H */

@@ -1,0 +1,139 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and its argument checks and planning (pure host code) behave as
+documented in include/tgemm.h. No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tiled_gemm_output_amd import tgemm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tgemm.h")
+
+NN = ctypes.c_void_p(0x1000)  # a non-null pointer value; never dereferenced by host code
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tgemm.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert declared == sorted(tgemm.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert tgemm.gemm_status_string(s).startswith("GEMM_")
+    assert tgemm.gemm_status_string(99) == "unknown status"
+
+
+def ok_args(M=64, N=48, K=32):
+    return [M, N, K, NN, K, NN, N, NN, N]
+
+
+@pytest.mark.parametrize("dtype", range(5))
+def test_valid_args(dtype):
+    assert tgemm.gemm_check_args(*ok_args(), dtype) == tgemm.OK
+
+
+@pytest.mark.parametrize(
+    "patch,expected",
+    [
+        ({0: -1}, tgemm.ERR_INVALID_ARG),            # M < 0
+        ({1: -5}, tgemm.ERR_INVALID_ARG),            # N < 0
+        ({2: -1}, tgemm.ERR_INVALID_ARG),            # K < 0
+        ({4: 31}, tgemm.ERR_INVALID_ARG),            # lda < K
+        ({6: 47}, tgemm.ERR_INVALID_ARG),            # ldb < N
+        ({8: 47}, tgemm.ERR_INVALID_ARG),            # ldc < N
+        ({3: None}, tgemm.ERR_INVALID_ARG),          # A null with elements
+        ({5: None}, tgemm.ERR_INVALID_ARG),          # B null with elements
+        ({7: None}, tgemm.ERR_INVALID_ARG),          # C null with elements
+        ({0: 2**31}, tgemm.ERR_INVALID_ARG),         # dimension beyond int32
+    ],
+)
+def test_bad_args(patch, expected):
+    args = ok_args()
+    for i, v in patch.items():
+        args[i] = v
+    assert tgemm.gemm_check_args(*args, tgemm.BF16_BF16) == expected
+
+
+def test_unknown_dtype():
+    assert tgemm.gemm_check_args(*ok_args(), 5) == tgemm.ERR_UNSUPPORTED_DTYPE
+    assert tgemm.gemm_check_args(*ok_args(), -1) == tgemm.ERR_UNSUPPORTED_DTYPE
+
+
+def test_null_pointers_allowed_for_empty_matrices():
+    # M == 0: A and C have no elements
+    assert tgemm.gemm_check_args(0, 8, 8, None, 8, NN, 8, None, 8, tgemm.F16_F32) == tgemm.OK
+    # K == 0: A and B have no elements, C is zero-filled
+    assert tgemm.gemm_check_args(4, 8, 0, None, 1, None, 8, NN, 8, tgemm.F16_F32) == tgemm.OK
+    assert tgemm.gemm_check_args(4, 8, 0, None, 1, None, 8, None, 8, tgemm.F16_F32) == tgemm.ERR_INVALID_ARG
+
+
+def test_null_or_unknown_handle():
+    assert tgemm.gemm_destroy(None) == tgemm.ERR_INVALID_ARG
+    assert tgemm.gemm_set_tile(None, 16, 16, 32) == tgemm.ERR_INVALID_ARG
+    assert tgemm.gemm_run(None, *ok_args(), tgemm.BF16_BF16, None) == tgemm.ERR_INVALID_ARG
+    bogus = ctypes.c_void_p(0xDEADBEEF0)
+    assert tgemm.gemm_destroy(bogus) == tgemm.ERR_INVALID_ARG
+    assert tgemm.gemm_run(bogus, *ok_args(), tgemm.BF16_BF16, None) == tgemm.ERR_INVALID_ARG
+
+
+def test_create_without_gpu():
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    h = ctypes.c_void_p()
+    assert tgemm.load().gemm_create(ctypes.byref(h)) == tgemm.ERR_NO_DEVICE
+    assert tgemm.load().gemm_create(None) == tgemm.ERR_INVALID_ARG
+
+
+def plan(M, N, K, dtype, A=0x10000, lda=None, B=0x20000, ldb=None, ldc=None):
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return tgemm.gemm_plan(None, M, N, K, ctypes.c_void_p(A), max(lda, 1), ctypes.c_void_p(B), max(ldb, 1),
+                           ctypes.c_void_p(0x30000), max(ldc, 1), dtype)
+
+
+def test_plan_auto_tiles():
+    p = plan(8192, 8192, 8192, tgemm.BF16_BF16)
+    assert (p["tile_m"], p["tile_n"], p["tile_k"]) == (256, 256, 64)
+    assert p["kernel_name"] == "mfma_macro_tile" and p["vector_loads"] == 1 and p["grid"] == 32 * 32
+    p = plan(96, 96, 96, tgemm.BF16_F32)
+    assert p["kernel_name"] == "mfma_macro_tile" and p["vector_loads"] == 1
+    p = plan(9, 9, 9, tgemm.I32_I32)
+    assert p["kernel_name"] == "int32_valu"
+
+
+def test_plan_vector_loads_need_alignment():
+    assert plan(1000, 777, 333, tgemm.BF16_F32)["vector_loads"] == 0        # K, N not multiples of 8
+    assert plan(256, 256, 256, tgemm.BF16_F32, A=0x10002)["vector_loads"] == 0  # A not 16-byte aligned
+    assert plan(256, 256, 256, tgemm.BF16_F32, lda=260)["vector_loads"] == 0    # lda not a multiple of 8
+    assert plan(256, 256, 256, tgemm.BF16_F32, lda=264)["vector_loads"] == 1
+
+
+def test_plan_empty_and_zero_k():
+    assert plan(0, 16, 16, tgemm.BF16_F32)["kernel_name"] == "none"
+    assert plan(16, 0, 16, tgemm.BF16_F32)["kernel_name"] == "none"
+    assert plan(16, 16, 0, tgemm.BF16_F32)["kernel_name"] == "zero_fill"
+
+
+def test_plan_rejects_bad_arguments():
+    with pytest.raises(tgemm.GemmError) as e:
+        plan(-1, 16, 16, tgemm.BF16_F32)
+    assert e.value.status == tgemm.ERR_INVALID_ARG

@@ -1,0 +1,250 @@
+"""GPU parity: the HIP library (through its C ABI) against the oracle.
+
+Every case runs through gemm_run on the device and is compared with the oracle on
+the same seeded inputs (tiled_gemm_output_amd/inputs.py): bit-exact for int32 and
+for integer-valued float inputs, the accuracy rule of gpu_util otherwise. Full
+outputs are compared at the small workloads and a randomized sweep of ragged
+shapes, leading dimensions and pointer offsets; at the large workloads the
+sampled rows and columns (one per 128-block plus the first and last) are compared,
+in the same launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests import gpu_util as G
+from tests import oracle_pins
+from tiled_gemm_output_amd import inputs, tgemm
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def h():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    g = tgemm.gemm_create()
+    yield g
+    tgemm.gemm_destroy(g)
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.get()
+
+
+def set_tile(h, tile):
+    tgemm.check(tgemm.gemm_set_tile(h, *(tile or (0, 0, 0))), "gemm_set_tile")
+
+
+def oracle_ref(o, a, b, dtype):
+    return o.gemm(a, b, G.IN_KIND[dtype], G.OUT_KIND[dtype])
+
+
+def check_full(h, o, a, b, dtype, tile=None, **layout):
+    set_tile(h, tile)
+    try:
+        c, dc = G.run(h, a, b, dtype, **layout)
+    finally:
+        set_tile(h, None)
+    assert dc.untouched_outside(), "kernel wrote outside C"
+    ref = oracle_ref(o, a, b, dtype)
+    if dtype == tgemm.I32_I32:
+        return G.compare(c.view(np.int32), ref.view(np.int32), "i32")
+    return G.compare(c, ref.view(G.np_int(tgemm.OUT_BYTES[dtype])), G.OUT_KIND[dtype])
+
+
+# ---------------------------------------------------------------- the workloads
+
+def test_worked_example_9x9(h, o):
+    """The puzzle page's example with its 3x3 tiles: bit-exact, and equal to the closed form."""
+    a, b = inputs.worked_example()
+    for tile in [(3, 3, 3), None]:
+        set_tile(h, tile)
+        c, dc = G.run(h, a, b, tgemm.I32_I32)
+        set_tile(h, None)
+        assert dc.untouched_outside()
+        assert np.array_equal(c.astype(np.int64), oracle_pins.worked_closed_form())
+        assert np.array_equal(c, o.gemm(a, b, "i32", "i32"))
+
+
+def test_square128_f16_16x16x32(h, o):
+    w = inputs.WORKLOADS["square128_f16"]
+    a, b = inputs.make(w)
+    st = check_full(h, o, a, b, tgemm.F16_F32, tile=w.tile)
+    assert st["normwise"] < 1e-5
+    set_tile(h, w.tile)
+    p = tgemm.gemm_plan(h, 128, 128, 128, 1 << 20, 128, 1 << 21, 128, 1 << 22, 128, tgemm.F16_F32)
+    set_tile(h, None)
+    assert p["kernel_name"] == "mfma_16x16x32_one_wave" and p["grid"] == 64 and p["vector_loads"] == 1
+
+
+@pytest.mark.parametrize("name", ["ragged96_bf16", "ragged1000x777x333_bf16"])
+@pytest.mark.parametrize("dtype", [tgemm.BF16_F32, tgemm.BF16_BF16])
+@pytest.mark.parametrize("forced", [True, False])
+def test_ragged_edge_tiles(h, o, name, dtype, forced):
+    w = inputs.WORKLOADS[name]
+    a, b = inputs.make(w)
+    check_full(h, o, a, b, dtype, tile=w.tile if forced else None)
+
+
+LARGE = ["square4096_bf16", "square8192_bf16", "tall16384x1024x8192_bf16", "skinny128x8192x8192_bf16"]
+
+
+def sampled_check(h, o, a, b, dtype, rows, cols, exact=False):
+    """Run at full size; compare the sampled rows and columns with the oracle."""
+    import torch
+
+    M, K = a.shape
+    N = b.shape[1]
+    ob = tgemm.OUT_BYTES[dtype]
+    da = torch.from_numpy(a.view(np.int16)).cuda()
+    db = torch.from_numpy(b.view(np.int16)).cuda()
+    dc = torch.full((M, N), G.SENTINEL[ob], dtype=G.int_dtype(ob), device="cuda")
+    st = tgemm.gemm_run(h, M, N, K, da.data_ptr(), K, db.data_ptr(), N, dc.data_ptr(), N, dtype,
+                        torch.cuda.current_stream().cuda_stream)
+    tgemm.check(st, "gemm_run")
+    torch.cuda.synchronize()
+    kind_in, kind_out = G.IN_KIND[dtype], G.OUT_KIND[dtype]
+    got_r = dc[torch.from_numpy(rows).cuda()].cpu().numpy()
+    got_c = dc[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+    ref_r = o.gemm_rows(a, b, rows, kind_in, kind_out).view(G.np_int(ob))
+    ref_c = o.gemm_cols(a, b, cols, kind_in, kind_out).view(G.np_int(ob))
+    if exact:
+        assert np.array_equal(got_r, ref_r) and np.array_equal(got_c, ref_c)
+        return {}
+    s1 = G.compare(got_r, ref_r, kind_out)
+    s2 = G.compare(got_c, ref_c, kind_out)
+    return {"rows": s1, "cols": s2}
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_large_workloads_sampled(h, o, name):
+    w = inputs.WORKLOADS[name]
+    a, b = inputs.make(w)
+    rows, cols = inputs.sample_rows_cols(w.M, w.N, seed=w.index, block=256)
+    sampled_check(h, o, a, b, tgemm.DTYPES[w.dtype], rows, cols)
+
+
+@pytest.mark.parametrize("name", ["square8192_bf16", "skinny128x8192x8192_bf16"])
+def test_large_exact_integer_inputs(h, o, name):
+    """Integer-valued inputs in [-8, 8]: every fp32 partial sum is exact, so the
+    sampled outputs must match the oracle bit for bit at full size."""
+    w = inputs.WORKLOADS[name]
+    a = inputs.draw((w.M, w.K), "small_int", "bf16", 101)
+    b = inputs.draw((w.K, w.N), "small_int", "bf16", 102)
+    rows, cols = inputs.sample_rows_cols(w.M, w.N, seed=7, block=512)
+    sampled_check(h, o, a, b, tgemm.DTYPES[w.dtype], rows, cols, exact=True)
+
+
+# ---------------------------------------------------------------- exact classes
+
+TILES_FLOAT = [(16, 16, 32), (64, 64, 64), (128, 128, 64), (256, 128, 64), (256, 256, 64), None]
+
+
+@pytest.mark.parametrize("tile", TILES_FLOAT, ids=str)
+@pytest.mark.parametrize("shape", [(300, 200, 150), (256, 256, 256), (33, 520, 72), (1, 1, 1), (257, 129, 8)], ids=str)
+def test_integer_inputs_bit_exact(h, o, tile, shape):
+    M, N, K = shape
+    for dtype, kind in [(tgemm.BF16_F32, "bf16"), (tgemm.F16_F32, "f16"), (tgemm.BF16_BF16, "bf16")]:
+        a = inputs.draw((M, K), "small_int", kind, 11 + M)
+        b = inputs.draw((K, N), "small_int", kind, 13 + N)
+        set_tile(h, tile)
+        c, dc = G.run(h, a, b, dtype)
+        set_tile(h, None)
+        assert dc.untouched_outside()
+        ref = oracle_ref(o, a, b, dtype).view(G.np_int(tgemm.OUT_BYTES[dtype]))
+        assert np.array_equal(c, ref), (dtype, tile, shape)
+
+
+def test_identity_and_zero(h, o):
+    rng = np.random.default_rng(5)
+    a = inputs.to_bits(rng.standard_normal((130, 96)).astype(np.float32), "bf16")
+    eye = inputs.to_bits(np.eye(96, dtype=np.float32), "bf16")
+    c, _ = G.run(h, a, eye, tgemm.BF16_BF16)
+    assert np.array_equal(c.view(np.uint16), a)
+    z = np.zeros_like(a)
+    c, _ = G.run(h, z, eye, tgemm.BF16_F32)
+    assert not np.any(G.values(c, "f32"))
+
+
+# ---------------------------------------------------------------- sweep
+
+def sweep_cases():
+    rng = np.random.default_rng(2026)
+    cases = []
+    dtypes = [tgemm.BF16_F32, tgemm.BF16_BF16, tgemm.F16_F32, tgemm.F16_F16, tgemm.I32_I32]
+    for n in range(40):
+        M, N, K = (int(x) for x in rng.integers(1, 301, size=3))
+        dtype = dtypes[n % len(dtypes)]
+        pad = [0, 1, 8][n % 3]
+        offs = (0, 0, 0) if n % 4 == 0 else tuple(int(x) for x in rng.integers(0, 9, size=3))
+        cases.append((M, N, K, dtype, pad, offs))
+    # aligned shapes that take the direct-load path, and K not a multiple of 64
+    cases += [(512, 384, 200, tgemm.BF16_F32, 0, (0, 0, 0)), (520, 264, 136, tgemm.BF16_BF16, 8, (0, 0, 0)),
+              (1024, 1024, 64, tgemm.F16_F32, 0, (0, 0, 0)), (768, 512, 1000, tgemm.BF16_F32, 0, (0, 0, 0))]
+    return cases
+
+
+@pytest.mark.parametrize("case", sweep_cases(), ids=str)
+def test_random_sweep(h, o, case):
+    M, N, K, dtype, pad, offs = case
+    kind = G.IN_KIND[dtype]
+    a, b = inputs.random_case(M, N, K, kind, seed=M * 7 + N * 3 + K)
+    check_full(h, o, a, b, dtype, lda=K + pad, ldb=N + pad, ldc=N + pad, offs=offs)
+
+
+@pytest.mark.parametrize("tile", [(3, 3, 3), (1, 1, 1), (16, 16, 64), (32, 8, 7), (32, 32, 32), None], ids=str)
+def test_int32_tiles(h, o, tile):
+    a, b = inputs.random_case(77, 45, 61, "i32", seed=3)
+    check_full(h, o, a, b, tgemm.I32_I32, tile=tile)
+
+
+# ---------------------------------------------------------------- degenerate cases
+
+def test_k_zero_fills_zeros(h, o):
+    import torch
+
+    for dtype in [tgemm.BF16_F32, tgemm.BF16_BF16, tgemm.I32_I32]:
+        ob = tgemm.OUT_BYTES[dtype]
+        dc = G.DevMatrix(None, 37, 21, 24, 3, ob)
+        st = tgemm.gemm_run(h, 37, 21, 0, None, 1, None, 21, dc.ptr, dc.ld, dtype,
+                            torch.cuda.current_stream().cuda_stream)
+        tgemm.check(st)
+        torch.cuda.synchronize()
+        assert not np.any(dc.host()) and dc.untouched_outside()
+
+
+def test_empty_output_launches_nothing(h):
+    import torch
+
+    dc = G.DevMatrix(None, 4, 4, 4, 0, 4)
+    for M, N in [(0, 4), (4, 0)]:
+        st = tgemm.gemm_run(h, M, N, 5, dc.ptr, 5, dc.ptr, max(N, 1), dc.ptr, max(N, 1), tgemm.BF16_F32,
+                            torch.cuda.current_stream().cuda_stream)
+        assert st == tgemm.OK
+    torch.cuda.synchronize()
+    assert np.all(dc.host() == dc.fill)
+
+
+def test_unsupported_forced_tile(h):
+    tgemm.check(tgemm.gemm_set_tile(h, 48, 48, 48))
+    try:
+        st = tgemm.gemm_run(h, 64, 64, 64, 1 << 20, 64, 1 << 21, 64, 1 << 22, 64, tgemm.BF16_F32, None)
+        assert st == tgemm.ERR_UNSUPPORTED_TILE
+    finally:
+        tgemm.gemm_set_tile(h, 0, 0, 0)
+
+
+def test_repeatable_and_side_stream(h, o):
+    """Same inputs twice (second time on a non-default stream): identical bits."""
+    import torch
+
+    a, b = inputs.random_case(1024, 768, 1536, "bf16", seed=9)
+    c1, _ = G.run(h, a, b, tgemm.BF16_F32)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c2, _ = G.run(h, a, b, tgemm.BF16_F32, stream=s)
+    assert np.array_equal(c1, c2)
+    G.compare(c1, oracle_ref(o, a, b, tgemm.BF16_F32).view(np.int32), "f32")

@@ -1,0 +1,281 @@
+// api.hip -- the C ABI of include/tgemm.h: handles, argument checks, kernel
+// choice and launch. Argument errors are found here, on the host, before any HIP
+// call; launches are asynchronous on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <unordered_set>
+
+#include "launch.h"
+#include "tgemm.h"
+
+struct tgemm_handle {
+  int device;
+  int cus;
+  int tm, tn, tk;  // forced tile, 0 = automatic
+};
+
+namespace {
+
+std::mutex g_mu;
+std::unordered_set<const tgemm_handle*>& live() {
+  static std::unordered_set<const tgemm_handle*> s;
+  return s;
+}
+bool is_live(const tgemm_handle* h) {
+  std::lock_guard<std::mutex> g(g_mu);
+  return h != nullptr && live().count(h) != 0;
+}
+
+constexpr int64_t kI32Max = 0x7fffffffLL;
+constexpr int64_t kMaxRecords = 0x7FFFFFF0LL;  // must match device_common.h
+
+int out_bytes(int dtype) { return (dtype == GEMM_I32_I32 || dtype == GEMM_F16_F32 || dtype == GEMM_BF16_F32) ? 4 : 2; }
+int in_kind(int dtype) { return (dtype == GEMM_BF16_F32 || dtype == GEMM_BF16_BF16) ? 1 : 0; }  // 1 = bf16
+int out_kind(int dtype) {
+  if (dtype == GEMM_BF16_BF16) return 1;
+  if (dtype == GEMM_F16_F16) return 2;
+  return 0;
+}
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t max1(int64_t x) { return x > 1 ? x : 1; }
+
+// Can the tile's 16-byte buffer loads be used? Needs 16-byte aligned A and B, row
+// strides and the K and N extents in whole 8-element chunks, and every in-tile
+// offset below the buffer range limit.
+bool vector_ok(int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, int bm, int bn, int bk) {
+  if (((uintptr_t)A & 15) || ((uintptr_t)B & 15)) return false;
+  if ((lda & 7) || (ldb & 7) || (K & 7) || (N & 7)) return false;
+  if (((int64_t)(bm - 1) * lda + bk) * 2 >= kMaxRecords) return false;
+  if (((int64_t)(bk - 1) * ldb + bn) * 2 >= kMaxRecords) return false;
+  return true;
+}
+
+int find_macro(int tm, int tn, int tk) {
+  for (int i = 0; i < tg::kNumMacroShapes; ++i)
+    if (tg::kMacroShapes[i].bm == tm && tg::kMacroShapes[i].bn == tn && tg::kMacroShapes[i].bk == tk) return i;
+  return -1;
+}
+
+// Automatic tile: the largest macro tile that still gives the chip (256 CUs) a
+// full wave of workgroups; smaller tiles for smaller problems.
+int auto_macro(int64_t M, int64_t N) {
+  const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
+  if (t256 >= 256) return 0;
+  const int64_t t256x128 = cdiv(M, 256) * cdiv(N, 128);
+  if (t256x128 >= 256) return 1;
+  const int64_t t128 = cdiv(M, 128) * cdiv(N, 128);
+  if (t128 >= 64) return 2;
+  return 3;
+}
+
+gemm_status_t plan_impl(const tgemm_handle* h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                        const void* B, int64_t ldb, const void* C, int64_t ldc, int dtype, gemm_plan_t* out) {
+  gemm_status_t st = gemm_check_args(M, N, K, A, lda, B, ldb, C, ldc, (gemm_dtype_t)dtype);
+  if (st != GEMM_OK) return st;
+  gemm_plan_t p;
+  std::memset(&p, 0, sizeof(p));
+  const int ftm = h ? h->tm : 0, ftn = h ? h->tn : 0, ftk = h ? h->tk : 0;
+  const bool forced = ftm != 0;
+  if (dtype == GEMM_I32_I32) {
+    const int tm = forced ? ftm : 16, tn = forced ? ftn : 16, tk = forced ? ftk : 64;
+    if ((int64_t)tm * tn > 1024 || ((int64_t)tm * tk + (int64_t)tk * tn) * 4 > 65536) return GEMM_ERR_UNSUPPORTED_TILE;
+    p.tile_m = tm;
+    p.tile_n = tn;
+    p.tile_k = tk;
+    p.threads = tm * tn;
+    p.lds_bytes = (tm * tk + tk * tn) * 4;
+    p.vector_loads = 0;
+    p.kernel = 2;
+  } else {
+    int shape = -1;
+    bool small = false;
+    if (forced) {
+      if (ftm == 16 && ftn == 16 && ftk == 32)
+        small = true;
+      else if ((shape = find_macro(ftm, ftn, ftk)) < 0)
+        return GEMM_ERR_UNSUPPORTED_TILE;
+    } else {
+      shape = auto_macro(M, N);
+    }
+    if (small) {
+      p.tile_m = 16;
+      p.tile_n = 16;
+      p.tile_k = 32;
+      p.threads = 64;
+      p.lds_bytes = 4096;
+      p.kernel = 3;
+    } else {
+      const tg::MacroShape& s = tg::kMacroShapes[shape];
+      p.tile_m = s.bm;
+      p.tile_n = s.bn;
+      p.tile_k = s.bk;
+      p.threads = s.threads;
+      p.lds_bytes = s.lds;
+      p.kernel = 4;
+    }
+    p.vector_loads = vector_ok(N, K, A, lda, B, ldb, p.tile_m, p.tile_n, p.tile_k) ? 1 : 0;
+  }
+  if (M == 0 || N == 0) {
+    p.kernel = 0;
+    p.grid = 0;
+  } else if (K == 0) {
+    p.kernel = 1;
+    p.grid = cdiv(M * N, 256) < 65536 ? cdiv(M * N, 256) : 65536;
+  } else {
+    p.grid = cdiv(M, p.tile_m) * cdiv(N, p.tile_n);
+    if (p.grid > kI32Max) return GEMM_ERR_INVALID_ARG;
+  }
+  *out = p;
+  return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gemm_status_string(gemm_status_t s) {
+  switch (s) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG: invalid argument or handle";
+    case GEMM_ERR_UNSUPPORTED_DTYPE: return "GEMM_ERR_UNSUPPORTED_DTYPE: unknown dtype";
+    case GEMM_ERR_NO_DEVICE: return "GEMM_ERR_NO_DEVICE: no HIP device";
+    case GEMM_ERR_ARCH: return "GEMM_ERR_ARCH: device is not gfx950";
+    case GEMM_ERR_HIP: return "GEMM_ERR_HIP: HIP runtime or launch failure";
+    case GEMM_ERR_OUT_OF_MEMORY: return "GEMM_ERR_OUT_OF_MEMORY: host allocation failed";
+    case GEMM_ERR_UNSUPPORTED_TILE: return "GEMM_ERR_UNSUPPORTED_TILE: no kernel has this tile for this dtype";
+  }
+  return "unknown status";
+}
+
+gemm_status_t gemm_check_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                              int64_t ldb, const void* C, int64_t ldc, gemm_dtype_t dtype) {
+  const int d = (int)dtype;
+  if (d < GEMM_I32_I32 || d > GEMM_F16_F16) return GEMM_ERR_UNSUPPORTED_DTYPE;
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+  if (M > kI32Max || N > kI32Max || K > kI32Max) return GEMM_ERR_INVALID_ARG;
+  if (lda < max1(K) || ldb < max1(N) || ldc < max1(N)) return GEMM_ERR_INVALID_ARG;
+  if (lda > (int64_t)1 << 40 || ldb > (int64_t)1 << 40 || ldc > (int64_t)1 << 40) return GEMM_ERR_INVALID_ARG;
+  if (M * K > 0 && A == nullptr) return GEMM_ERR_INVALID_ARG;
+  if (K * N > 0 && B == nullptr) return GEMM_ERR_INVALID_ARG;
+  if (M * N > 0 && C == nullptr) return GEMM_ERR_INVALID_ARG;
+  return GEMM_OK;
+}
+
+gemm_status_t gemm_create(gemm_handle_t* out) {
+  if (out == nullptr) return GEMM_ERR_INVALID_ARG;
+  *out = nullptr;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return GEMM_ERR_NO_DEVICE;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_ERR_ARCH;
+  tgemm_handle* h = new (std::nothrow) tgemm_handle;
+  if (h == nullptr) return GEMM_ERR_OUT_OF_MEMORY;
+  h->device = dev;
+  h->cus = prop.multiProcessorCount;
+  h->tm = h->tn = h->tk = 0;
+  {
+    std::lock_guard<std::mutex> g(g_mu);
+    live().insert(h);
+  }
+  *out = h;
+  return GEMM_OK;
+}
+
+gemm_status_t gemm_destroy(gemm_handle_t h) {
+  {
+    std::lock_guard<std::mutex> g(g_mu);
+    if (h == nullptr || live().erase(h) == 0) return GEMM_ERR_INVALID_ARG;
+  }
+  delete h;
+  return GEMM_OK;
+}
+
+gemm_status_t gemm_set_tile(gemm_handle_t h, int32_t tm, int32_t tn, int32_t tk) {
+  if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
+  const bool all_zero = tm == 0 && tn == 0 && tk == 0;
+  if (!all_zero && (tm <= 0 || tn <= 0 || tk <= 0)) return GEMM_ERR_INVALID_ARG;
+  h->tm = tm;
+  h->tn = tn;
+  h->tk = tk;
+  return GEMM_OK;
+}
+
+gemm_status_t gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                        const void* B, int64_t ldb, const void* C, int64_t ldc, gemm_dtype_t dtype,
+                        gemm_plan_t* out) {
+  if (out == nullptr) return GEMM_ERR_INVALID_ARG;
+  if (h != nullptr && !is_live(h)) return GEMM_ERR_INVALID_ARG;
+  return plan_impl(h, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, out);
+}
+
+gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, void* C, int64_t ldc, gemm_dtype_t dtype, void* stream) {
+  if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
+  gemm_plan_t p;
+  gemm_status_t st = plan_impl(h, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &p);
+  if (st != GEMM_OK) return st;
+  static const bool log = std::getenv("TGEMM_LOG") != nullptr;
+  if (log)
+    std::fprintf(stderr, "tgemm: M=%lld N=%lld K=%lld dtype=%d kernel=%d tile=%dx%dx%d threads=%d vec=%d grid=%lld\n",
+                 (long long)M, (long long)N, (long long)K, (int)dtype, p.kernel, p.tile_m, p.tile_n, p.tile_k,
+                 p.threads, p.vector_loads, (long long)p.grid);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  switch (p.kernel) {
+    case 0: return GEMM_OK;
+    case 1: e = tg::launch_zero_fill(C, M, N, ldc, out_bytes(dtype), s); break;
+    case 2: {
+      tg::I32Args a;
+      a.A = (const int32_t*)A;
+      a.B = (const int32_t*)B;
+      a.C = (int32_t*)C;
+      a.M = (int)M;
+      a.N = (int)N;
+      a.K = (int)K;
+      a.lda = lda;
+      a.ldb = ldb;
+      a.ldc = ldc;
+      a.tm = p.tile_m;
+      a.tn = p.tile_n;
+      a.tk = p.tile_k;
+      a.tiles_n = (int)cdiv(N, p.tile_n);
+      e = tg::launch_i32(a, s, p.grid, p.threads, p.lds_bytes);
+      break;
+    }
+    default: {
+      tg::MacroArgs a;
+      a.A = (const uint16_t*)A;
+      a.B = (const uint16_t*)B;
+      a.C = C;
+      a.M = (int)M;
+      a.N = (int)N;
+      a.K = (int)K;
+      a.lda = lda;
+      a.ldb = ldb;
+      a.ldc = ldc;
+      a.tiles_m = (int)cdiv(M, p.tile_m);
+      a.tiles_n = (int)cdiv(N, p.tile_n);
+      a.group_m = a.tiles_m < 8 ? a.tiles_m : 8;
+      if (p.kernel == 3)
+        e = tg::launch_small(a, in_kind(dtype), out_kind(dtype), p.vector_loads != 0, s, p.grid);
+      else
+        e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k), a, in_kind(dtype), out_kind(dtype),
+                             p.vector_loads != 0, s, p.grid);
+      break;
+    }
+  }
+  return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// launch.h -- kernel argument blocks and launchers (host side of the kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+// Arguments of the MFMA kernels. Dimensions fit in int32 (checked by the host).
+struct MacroArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  void* C;
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+  int tiles_m, tiles_n, group_m;
+};
+
+struct MacroShape {
+  int bm, bn, bk, threads, lds;
+};
+constexpr int kNumMacroShapes = 5;
+extern const MacroShape kMacroShapes[kNumMacroShapes];
+
+// in: 0 = f16, 1 = bf16. out: 0 = f32, 1 = bf16, 2 = f16.
+hipError_t launch_macro(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid);
+hipError_t launch_small(const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid);
+
+struct I32Args {
+  const int32_t* A;
+  const int32_t* B;
+  int32_t* C;
+  int M, N, K;
+  int64_t lda, ldb, ldc;
+  int tm, tn, tk, tiles_n;
+};
+hipError_t launch_i32(const I32Args& a, hipStream_t s, int64_t grid, int threads, int lds_bytes);
+
+// C[0:M, 0:N] = 0 for element size 2 or 4 bytes.
+hipError_t launch_zero_fill(void* C, int64_t M, int64_t N, int64_t ldc, int elem_bytes, hipStream_t s);
+
+}  // namespace tg
