@@ -111,6 +111,9 @@ def main() -> int:
     ap.add_argument("--tile", default=None, help="force a tile, e.g. 256,256,64")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain device copy of 1 GiB (5 times): the known-size kernel whose "
+                         "FETCH_SIZE / WRITE_SIZE readings scale the GEMM's counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py: this build runs on one GPU only; --gpus %d is not supported. "
@@ -130,6 +133,15 @@ def main() -> int:
         log("bench.py: no GPU visible")
         return 1
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        return 0
     w = inputs.WORKLOADS[args.workload]
     dtype = tgemm.DTYPES[w.dtype]
     log("bench: workload %s M=%d N=%d K=%d dtype=%s" % (w.name, w.M, w.N, w.K, w.dtype))

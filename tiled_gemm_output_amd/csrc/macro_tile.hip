@@ -65,27 +65,58 @@ __device__ __forceinline__ int swz_b(int k) {
   return h & (CH - 1);
 }
 
-// Direct-load geometry: DMA block t of a wave writes 1 KiB of LDS. For A (8 rows
-// of 128 bytes per block) lane l fills row blk*8 + l/8, physical chunk l%8, i.e.
-// logical chunk (l%8) ^ swz_a(row); for B (1024 / (2*BN) rows per block) lane l
-// fills row blk*rows + l / chunks, physical chunk l % chunks.
-#define A_DMA_HELPERS(Cfg)                                                                     \
-  auto a_dma_row = [&](int w, int t, int l) { return (w * kAPer + t) * 8 + (l >> 3); };       \
-  auto a_dma_chunk = [&](int r, int l) { return (l & 7) ^ swz_a(r); };                        \
-  auto b_dma_row = [&](int w, int t, int l) {                                                  \
-    return (w * kBPer + t) * Cfg::kBRowsPerBlock + l / Cfg::kBChunks;                          \
-  };                                                                                           \
-  auto b_dma_chunk = [&](int k, int l) { return (l % Cfg::kBChunks) ^ swz_b<Cfg::kBChunks>(k); };
-
-// LOAD: kLoadElem = guarded element loads; kLoadVec = 16-byte direct loads, the last
-// K-tile may be partial; kLoadVecFull = 16-byte direct loads, K is a multiple of BK.
+// Loads: kLoadElem = guarded element loads staged in registers; kLoadVec = 16-byte
+// direct loads, the last K-tile may be partial; kLoadVecFull = 16-byte direct loads,
+// K is a multiple of BK.
 enum { kLoadElem = 0, kLoadVec = 1, kLoadVecFull = 2 };
+
+template <int N>
+struct IC {
+  static constexpr int value = N;
+};
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IC<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Workgroup barrier without a memory fence. The waits the pipeline needs are
+// explicit s_waitcnt instructions placed before it (a fenced barrier would also
+// wait for every load in flight); the empty asm statements keep the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Instruction order inside one scheduling region: each MFMA is followed by the
+// next share of the region's LDS reads and global loads, so that reads for the
+// next substep and refill loads are issued early and spread over the MFMAs.
+template <int NM, int NR, int NV>
+__device__ __forceinline__ void interleave() {
+  constexpr int rper = NM > 0 ? (NR + NM - 1) / NM : 0;
+  constexpr int vper = NM > 0 ? (NV + NM - 1) / NM : 0;
+  static_for<0, NM>([&](auto q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    constexpr int r = NR - q.value * rper;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r < rper ? r : rper, 0);  // DS read
+    constexpr int v = NV - q.value * vper;
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v < vper ? v : vper, 0);  // VMEM read
+  });
+}
 
 template <class Cfg, int IN, int OUT, int LOAD>
 __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs p) {
   constexpr bool VEC = LOAD != kLoadElem;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
   constexpr int FM = Cfg::kFM, FN = Cfg::kFN;
+  constexpr int kAPer = Cfg::kABlocks / Cfg::kWaves;  // 1 KiB blocks per wave and stage
+  constexpr int kBPer = Cfg::kBBlocks / Cfg::kWaves;
+  constexpr int NR = FM + 2 * FN;  // LDS reads per substep
+  constexpr int NM = FM * FN;      // MFMAs per substep
   __shared__ __attribute__((aligned(1024))) char sA0[Cfg::kABytes];
   __shared__ __attribute__((aligned(1024))) char sA1[Cfg::kABytes];
   __shared__ __attribute__((aligned(1024))) char sB0[Cfg::kBBytes];
@@ -103,136 +134,100 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   const int64_t lda = p.lda, ldb = p.ldb;
   const int nk = (K + BK - 1) / BK;
 
-  // ---------------- loader state ----------------
-  constexpr int kAPer = Cfg::kABlocks / Cfg::kWaves;  // DMA blocks (or register chunks) per wave / thread
-  constexpr int kBPer = Cfg::kBBlocks / Cfg::kWaves;
-  A_DMA_HELPERS(Cfg)
-  // vector path: per-lane byte offsets relative to the step's base
-  uint32_t a_off[kAPer];
-  uint32_t b_off[kBPer];
-  // element path: each thread stages kAPer + kBPer chunks of 8 values in registers
-  i32x4 a_reg[kAPer], b_reg[kBPer];
-  uint32_t a_lds[kAPer], b_lds[kBPer];
-  int a_r[kAPer], a_c[kAPer], b_k[kBPer], b_c[kBPer];
+  // ---------------- loader geometry ----------------
+  // Block t of a wave fills 1 KiB of a stage. A: 8 rows of 128 bytes per block;
+  // lane l fills row blk*8 + l/8 at physical chunk l%8, i.e. logical chunk
+  // (l%8) ^ swz_a(row). B: 1024 / (2*BN) rows per block; lane l fills row
+  // blk*rows + l/chunks at physical chunk l%chunks. The direct loads write lane
+  // l's 16 bytes to block base + 16*l; the element path writes the same slot.
+  auto a_row = [&](int t, int l) { return (wave * kAPer + t) * 8 + (l >> 3); };
+  auto a_chunk = [&](int r, int l) { return (l & 7) ^ swz_a(r); };
+  auto b_row = [&](int t, int l) { return (wave * kBPer + t) * Cfg::kBRowsPerBlock + l / Cfg::kBChunks; };
+  auto b_chunk = [&](int k, int l) { return (l % Cfg::kBChunks) ^ swz_b<Cfg::kBChunks>(k); };
 
+  uint32_t a_off[kAPer], b_off[kBPer];  // byte offsets from the K-tile's origin, vector path
   if constexpr (VEC) {
 #pragma unroll
     for (int t = 0; t < kAPer; ++t) {
-      const int r = a_dma_row(wave, t, lane);
-      const int c = a_dma_chunk(r, lane);
-      a_off[t] = (row0 + r < M) ? (uint32_t)(((int64_t)r * lda + 8 * c) * 2) : kOutOfRange;
+      const int r = a_row(t, lane);
+      a_off[t] = (row0 + r < M) ? (uint32_t)(((int64_t)r * lda + 8 * a_chunk(r, lane)) * 2) : kOutOfRange;
     }
 #pragma unroll
     for (int t = 0; t < kBPer; ++t) {
-      const int k = b_dma_row(wave, t, lane);
-      const int c = b_dma_chunk(k, lane);
+      const int k = b_row(t, lane);
+      const int c = b_chunk(k, lane);
       b_off[t] = (col0 + 8 * c < N) ? (uint32_t)(((int64_t)k * ldb + 8 * c) * 2) : kOutOfRange;
     }
-  } else {
-#pragma unroll
-    for (int t = 0; t < kAPer; ++t) {
-      const int q = t * Cfg::kThreads + tid;  // chunk id within the A tile
-      const int r = q / Cfg::kAChunks, c = q % Cfg::kAChunks;
-      a_r[t] = r;
-      a_c[t] = c;
-      a_lds[t] = (uint32_t)(r * Cfg::kARow + ((c ^ swz_a(r)) << 4));
-    }
-#pragma unroll
-    for (int t = 0; t < kBPer; ++t) {
-      const int q = t * Cfg::kThreads + tid;
-      const int k = q / Cfg::kBChunks, c = q % Cfg::kBChunks;
-      b_k[t] = k;
-      b_c[t] = c;
-      b_lds[t] = (uint32_t)(k * Cfg::kBRow + ((c ^ swz_b<Cfg::kBChunks>(k)) << 4));
-    }
   }
-
   const uint16_t* gA = p.A + (int64_t)row0 * lda;
   const uint16_t* gB = p.B + col0;
 
-  // Issue the loads of K-tile kt into stage (sa, sb).
-  auto load_tile = [&](TG_LDS char* sa, TG_LDS char* sb, int kt) {
-    const int k0 = kt * BK;
-    if (kt < 0) {  // the prepended zero tile
-      if constexpr (VEC) {
-        const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.A, 0);
+  // Vector path: issue the direct loads of K-tile kt into a stage. Branch-free: a
+  // K-tile outside [0, nk) gets a zero-length buffer, so every lane reads zeros and
+  // no memory is touched (this keeps the compiler's tracking of which stage each
+  // load writes exact, so it adds no waits before reads of the other stage).
+  auto issue_loads = [&](TG_LDS char* sa, TG_LDS char* sb, int kt) {
+    const bool ok = (unsigned)kt < (unsigned)nk;
+    const int k0 = ok ? kt * BK : 0;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(gA + k0, ok ? ((int64_t)(M - 1 - row0) * lda + (K - k0)) * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(gB + (int64_t)k0 * ldb, ok ? ((int64_t)(K - 1 - k0) * ldb + (N - col0)) * 2 : 0);
 #pragma unroll
-        for (int t = 0; t < kAPer; ++t) load_lds_x4(rz, sa + (wave * kAPer + t) * 1024, kOutOfRange);
-#pragma unroll
-        for (int t = 0; t < kBPer; ++t) load_lds_x4(rz, sb + (wave * kBPer + t) * 1024, kOutOfRange);
-      } else {
-#pragma unroll
-        for (int t = 0; t < kAPer; ++t) a_reg[t] = i32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int t = 0; t < kBPer; ++t) b_reg[t] = i32x4{0, 0, 0, 0};
-      }
-      return;
+    for (int t = 0; t < kAPer; ++t) {
+      uint32_t off = a_off[t];
+      if constexpr (LOAD == kLoadVec) off = (k0 + 8 * a_chunk(a_row(t, lane), lane) < K) ? off : kOutOfRange;
+      load_lds_x4(ra, sa + (wave * kAPer + t) * 1024, off);
     }
-    if constexpr (VEC) {
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(gA + k0, ((int64_t)(M - 1 - row0) * lda + (K - k0)) * 2);
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(gB + (int64_t)k0 * ldb, ((int64_t)(K - 1 - k0) * ldb + (N - col0)) * 2);
-      if (LOAD == kLoadVecFull || k0 + BK <= K) {
 #pragma unroll
-        for (int t = 0; t < kAPer; ++t) load_lds_x4(ra, sa + (wave * kAPer + t) * 1024, a_off[t]);
-#pragma unroll
-        for (int t = 0; t < kBPer; ++t) load_lds_x4(rb, sb + (wave * kBPer + t) * 1024, b_off[t]);
-      } else {
-        // partial last K-tile: chunks at or beyond K read zeros
-        int ln = lane;
-        asm volatile("" : "+v"(ln));  // keep this tail-only arithmetic out of the main loop
-#pragma unroll
-        for (int t = 0; t < kAPer; ++t) {
-          const int kc = 8 * a_dma_chunk(a_dma_row(wave, t, ln), ln);
-          load_lds_x4(ra, sa + (wave * kAPer + t) * 1024, (k0 + kc < K) ? a_off[t] : kOutOfRange);
-        }
-#pragma unroll
-        for (int t = 0; t < kBPer; ++t) {
-          const int kr = b_dma_row(wave, t, ln);
-          load_lds_x4(rb, sb + (wave * kBPer + t) * 1024, (k0 + kr < K) ? b_off[t] : kOutOfRange);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < kAPer; ++t) {
-        const int gr = row0 + a_r[t];
-        const int gk = k0 + 8 * a_c[t];
-        const uint16_t* src = p.A + (int64_t)gr * lda + gk;
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = (gr < M && gk + 2 * e < K) ? src[2 * e] : 0u;
-          const uint32_t hi = (gr < M && gk + 2 * e + 1 < K) ? src[2 * e + 1] : 0u;
-          w[e] = lo | (hi << 16);
-        }
-        a_reg[t] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-      }
-#pragma unroll
-      for (int t = 0; t < kBPer; ++t) {
-        const int gk = k0 + b_k[t];
-        const int gc = col0 + 8 * b_c[t];
-        const uint16_t* src = p.B + (int64_t)gk * ldb + gc;
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = (gk < K && gc + 2 * e < N) ? src[2 * e] : 0u;
-          const uint32_t hi = (gk < K && gc + 2 * e + 1 < N) ? src[2 * e + 1] : 0u;
-          w[e] = lo | (hi << 16);
-        }
-        b_reg[t] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-      }
+    for (int t = 0; t < kBPer; ++t) {
+      uint32_t off = b_off[t];
+      if constexpr (LOAD == kLoadVec) off = (k0 + b_row(t, lane) < K) ? off : kOutOfRange;
+      load_lds_x4(rb, sb + (wave * kBPer + t) * 1024, off);
     }
   };
 
-  // Make the stage's data visible: wait for the direct loads, or write the staged registers.
-  auto commit_tile = [&](TG_LDS char* sa, TG_LDS char* sb) {
-    if constexpr (VEC) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS-DMA writes have landed
-    } else {
+  // Element path: guarded 16-bit loads of K-tile kt into registers (zeros outside
+  // the matrices and for kt outside [0, nk)), and their 16-byte LDS writes.
+  i32x4 a_reg[kAPer], b_reg[kBPer];
+  auto fetch_regs = [&](int kt) {
+    const bool ok = (unsigned)kt < (unsigned)nk;
+    const int k0 = kt * BK;
 #pragma unroll
-      for (int t = 0; t < kAPer; ++t) *(TG_LDS i32x4*)(sa + a_lds[t]) = a_reg[t];
+    for (int t = 0; t < kAPer; ++t) {
+      const int r = a_row(t, lane);
+      const int gr = row0 + r, gk = k0 + 8 * a_chunk(r, lane);
+      const bool rv = ok && gr < M;
+      const uint16_t* src = p.A + (int64_t)gr * lda + gk;
+      uint32_t w[4];
 #pragma unroll
-      for (int t = 0; t < kBPer; ++t) *(TG_LDS i32x4*)(sb + b_lds[t]) = b_reg[t];
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = (rv && gk + 2 * e < K) ? src[2 * e] : 0u;
+        const uint32_t hi = (rv && gk + 2 * e + 1 < K) ? src[2 * e + 1] : 0u;
+        w[e] = lo | (hi << 16);
+      }
+      a_reg[t] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     }
+#pragma unroll
+    for (int t = 0; t < kBPer; ++t) {
+      const int k = b_row(t, lane);
+      const int gk = k0 + k, gc = col0 + 8 * b_chunk(k, lane);
+      const bool kv = ok && gk < K;
+      const uint16_t* src = p.B + (int64_t)gk * ldb + gc;
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = (kv && gc + 2 * e < N) ? src[2 * e] : 0u;
+        const uint32_t hi = (kv && gc + 2 * e + 1 < N) ? src[2 * e + 1] : 0u;
+        w[e] = lo | (hi << 16);
+      }
+      b_reg[t] = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    }
+  };
+  auto store_regs = [&](TG_LDS char* sa, TG_LDS char* sb) {
+#pragma unroll
+    for (int t = 0; t < kAPer; ++t) *(TG_LDS i32x4*)(sa + (wave * kAPer + t) * 1024 + lane * 16) = a_reg[t];
+#pragma unroll
+    for (int t = 0; t < kBPer; ++t) *(TG_LDS i32x4*)(sb + (wave * kBPer + t) * 1024 + lane * 16) = b_reg[t];
   };
 
   // ---------------- fragment addressing ----------------
@@ -262,46 +257,35 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-  // Fragments of substep s (16 reduction indices) of one stage.
-  auto read_frags = [&](TG_LDS char* sa, TG_LDS char* sb, int s, i32x4(&a)[FM], i32x4(&b)[FN]) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      // the substep selects chunk pair (2s, 2s+1); under the XOR swizzle that is an
-      // XOR of the byte address with s << 5 (computed here, not hoisted out of the loop)
-      uint32_t off = a_frag[i];
-      asm volatile("" : "+v"(off));
-      a[i] = *(TG_LDS i32x4*)(sa + (off ^ (uint32_t)(s << 5)));
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS s16x4*)(sb + b_frag[j] + (16 * s) * Cfg::kBRow));
-      const s16x4 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS s16x4*)(sb + b_frag[j] + (16 * s + 4) * Cfg::kBRow));
-      const int2 l2 = __builtin_bit_cast(int2, lo), h2 = __builtin_bit_cast(int2, hi);
-      b[j] = i32x4{l2.x, l2.y, h2.x, h2.y};
-    }
+  // Fragments of substep s (16 reduction indices), read in the order the MFMAs
+  // (row-major over the i x j blocks) consume them: a[0], every b[j], a[1..].
+  auto read_a = [&](TG_LDS char* sa, int s, int i) {
+    // the substep selects chunk pair (2s, 2s+1); under the XOR swizzle that is an
+    // XOR of the byte address with s << 5 (kept in the loop, not hoisted)
+    uint32_t off = a_frag[i];
+    asm volatile("" : "+v"(off));
+    return *(TG_LDS i32x4*)(sa + (off ^ (uint32_t)(s << 5)));
   };
-  auto mfma_all = [&](const i32x4(&a)[FM], const i32x4(&b)[FN]) {
+  auto read_b = [&](TG_LDS char* sb, int s, int j) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS s16x4*)(sb + b_frag[j] + (16 * s) * Cfg::kBRow));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS s16x4*)(sb + b_frag[j] + (16 * s + 4) * Cfg::kBRow));
+    const int2 l2 = __builtin_bit_cast(int2, lo), h2 = __builtin_bit_cast(int2, hi);
+    return i32x4{l2.x, l2.y, h2.x, h2.y};
+  };
+  auto read_frags = [&](TG_LDS char* sa, TG_LDS char* sb, int s, i32x4(&a)[FM], i32x4(&b)[FN]) {
+    a[0] = read_a(sa, s, 0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b[j] = read_b(sb, s, j);
+#pragma unroll
+    for (int i = 1; i < FM; ++i) a[i] = read_a(sa, s, i);
+  };
+  // MFMAs of one substep; half 0 = block rows [0, FM/2), half 1 = the rest.
+  auto mfma_rows = [&](const i32x4(&a)[FM], const i32x4(&b)[FN], int i0, int i1) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
+      if (i >= i0 && i < i1)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<IN>(a[i], b[j], acc[i][j]);
-  };
-  // Software pipeline over the substeps: the reads of substep s+1 are issued in the
-  // same scheduling region as the MFMAs of substep s; sched_barrier keeps regions
-  // apart so that at most two substeps' fragments are live.
-  auto compute_tile = [&](TG_LDS char* sa, TG_LDS char* sb) {
-    i32x4 a0[FM], b0[FN], a1[FM], b1[FN];
-    read_frags(sa, sb, 0, a0, b0);
-#pragma unroll
-    for (int s = 0; s < Cfg::kSubsteps; s += 2) {
-      read_frags(sa, sb, s + 1, a1, b1);
-      mfma_all(a0, b0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (s + 2 < Cfg::kSubsteps) read_frags(sa, sb, s + 2, a0, b0);
-      mfma_all(a1, b1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<IN>(a[i], b[j], acc[i][j]);
   };
 
   TG_LDS char* pA0 = (TG_LDS char*)sA0;
@@ -309,27 +293,70 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   TG_LDS char* pB0 = (TG_LDS char*)sB0;
   TG_LDS char* pB1 = (TG_LDS char*)sB1;
 
-  // ---------------- main loop: two stages, one barrier per K-step ----------------
-  // K-tiles are processed in pairs (stage 0, stage 1) so that every compute call
-  // is unconditional. When the number of K-tiles is odd, a zero tile (index -1,
-  // every load out of range, so no memory is read) is prepended: it adds exact
-  // zeros to the accumulator.
+  // ---------------- main loop ----------------
+  // Two stages; K-tile kt0 + st lives in stage st % 2. Each step multiplies its
+  // stage in four substeps; the reads of substep s+1 are issued among the MFMAs
+  // of substep s. The barrier that ends the step sits after the first half of the
+  // last substep's MFMAs: once every wave is past it, the stage just consumed is
+  // refilled with K-tile st + 2 and the next stage's first fragments are read,
+  // both covered by the second half of those MFMAs. When the number of K-tiles is
+  // odd, a zero K-tile (index -1) is prepended so that every step is unconditional.
   const int kt0 = (nk & 1) ? -1 : 0;
-  const int npairs = (nk - kt0) >> 1;
-  load_tile(pA0, pB0, kt0);
-  commit_tile(pA0, pB0);
-  __syncthreads();
-  for (int pr = 0, kt = kt0; pr < npairs; ++pr, kt += 2) {
-    load_tile(pA1, pB1, kt + 1);
-    compute_tile(pA0, pB0);
-    commit_tile(pA1, pB1);
-    __syncthreads();
-    const bool more = pr + 1 < npairs;
-    if (more) load_tile(pA0, pB0, kt + 2);
-    compute_tile(pA1, pB1);
-    if (more) commit_tile(pA0, pB0);
-    __syncthreads();
+  const int nsteps = nk - kt0;  // even, >= 2
+  i32x4 fa[FM], fb[FN], ga[FM], gb[FN];
+  if constexpr (VEC) {
+    issue_loads(pA0, pB0, kt0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  } else {
+    fetch_regs(kt0);
+    store_regs(pA0, pB0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   }
+  barrier_nofence();
+  if constexpr (VEC)
+    issue_loads(pA1, pB1, kt0 + 1);
+  else
+    fetch_regs(kt0 + 1);
+  read_frags(pA0, pB0, 0, fa, fb);
+
+  auto step = [&](TG_LDS char* sa, TG_LDS char* sb, TG_LDS char* na, TG_LDS char* nb, int st) {
+    read_frags(sa, sb, 1, ga, gb);
+    mfma_rows(fa, fb, 0, FM);
+    interleave<NM, NR, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(sa, sb, 2, fa, fb);
+    mfma_rows(ga, gb, 0, FM);
+    interleave<NM, NR, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(sa, sb, 3, ga, gb);
+    mfma_rows(fa, fb, 0, FM);
+    interleave<NM, NR, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_rows(ga, gb, 0, FM / 2);
+    __builtin_amdgcn_sched_barrier(0);
+    // the next stage must be complete in every wave before anyone reads it
+    if constexpr (VEC) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of K-tile st + 1 landed
+    } else {
+      store_regs(na, nb);                  // K-tile st + 1, fetched one step ago
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    }
+    barrier_nofence();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (VEC)
+      issue_loads(sa, sb, kt0 + st + 2);  // out of range on the last two steps: zero-length, no traffic
+    else
+      fetch_regs(kt0 + st + 2);
+    read_frags(na, nb, 0, fa, fb);
+    mfma_rows(ga, gb, FM / 2, FM);
+    interleave<(FM - FM / 2) * FN, NR, VEC ? kAPer + kBPer : 0>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int st = 0; st < nsteps; st += 2) {
+    step(pA0, pB0, pA1, pB1, st);
+    step(pA1, pB1, pA0, pB0, st + 1);
+  }
+  if constexpr (VEC) __builtin_amdgcn_s_waitcnt(0x0F70);  // trailing loads land before LDS is released
 
   // ---------------- epilogue: write the C tile once ----------------
   // acc[i][j][v] holds row 32i + 8*(v/4) + 4*(lane/32) + v%4, column 32j + lane%32
