@@ -109,6 +109,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="square8192_bf16")
     ap.add_argument("--tile", default=None, help="force a tile, e.g. 256,256,64")
+    ap.add_argument("--split-k", type=int, default=0, help="force the K-slice count (0: the library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -153,6 +154,7 @@ def main() -> int:
     h = tgemm.gemm_create()
     if args.tile:
         tgemm.check(tgemm.gemm_set_tile(h, *[int(x) for x in args.tile.split(",")]))
+    tgemm.check(tgemm.gemm_set_split_k(h, args.split_k), "gemm_set_split_k")
     plan = tgemm.gemm_plan(h, w.M, w.N, w.K, da.data_ptr(), w.K, db.data_ptr(), w.N, dc.data_ptr(), w.N, dtype)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -215,7 +217,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.in_kind, "acc": "fp32" if ib == 2 else "i32",
                    "out": w.out_kind, "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
-                   "kernel": plan["kernel_name"], "grid": plan["grid"], "threads": plan["threads"],
+                   "kernel": plan["kernel_name"], "grid": plan["grid"], "split_k": plan["split_k"],
+                   "threads": plan["threads"],
                    "vector_loads": plan["vector_loads"], "kernel_source_sha": sha},
         "pct_of_mfma_peak": 100.0 * value / PEAK_MFMA_16BIT_TFLOPS,
         "roofline": roof,

@@ -54,7 +54,7 @@ typedef enum {
   GEMM_ERR_NO_DEVICE = 3,         /* no HIP device visible */
   GEMM_ERR_ARCH = 4,              /* current device is not gfx950 */
   GEMM_ERR_HIP = 5,               /* a HIP runtime call or kernel launch failed */
-  GEMM_ERR_OUT_OF_MEMORY = 6,     /* host allocation of the handle failed */
+  GEMM_ERR_OUT_OF_MEMORY = 6,     /* allocation of the handle or of its split-K workspace failed */
   GEMM_ERR_UNSUPPORTED_TILE = 7   /* gemm_set_tile asked for a tile no kernel has, for this dtype */
 } gemm_status_t;
 
@@ -74,9 +74,10 @@ typedef struct {
   int32_t vector_loads;           /* 1: 16-byte loads straight into LDS; 0: element-wise loader */
   int32_t kernel;                 /* 0 none (empty C), 1 zero fill (K = 0), 2 int32 VALU,
                                      3 one-wave 16x16x32 MFMA, 4 macro-tile MFMA */
-  int64_t grid;                   /* workgroups launched */
+  int64_t grid;                   /* C tiles (workgroups per K-slice) */
   int32_t lds_bytes;              /* LDS per workgroup */
-  int32_t reserved;
+  int32_t split_k;                /* K-slices: 1, or S > 1 when each tile's reduction is cut into S
+                                     slices whose fp32 partial tiles a second kernel sums in slice order */
 } gemm_plan_t;
 
 /* Create a handle on the CURRENT HIP device. Host-only: no device work is enqueued.
@@ -95,11 +96,21 @@ gemm_status_t gemm_create(gemm_handle_t* out);
  *   dtype      one of gemm_dtype_t; element sizes: 4 (i32), 2 (f16, bf16) for A/B;
  *              4 for *_F32 and I32 outputs, 2 for *_BF16 and *_F16 outputs.
  * Errors: GEMM_ERR_INVALID_ARG, GEMM_ERR_UNSUPPORTED_DTYPE, GEMM_ERR_UNSUPPORTED_TILE
- * (a forced tile this dtype has no kernel for), GEMM_ERR_HIP (launch failed). */
+ * (a forced tile this dtype has no kernel for), GEMM_ERR_OUT_OF_MEMORY (split-K workspace),
+ * GEMM_ERR_HIP (launch failed).
+ * Split-K: with the automatic tile choice, a product whose C tiles cannot fill half
+ * of the GPU and whose K is long is computed in K-slices (gemm_plan reports split_k).
+ * The fp32 partial tiles go to a device workspace owned by the handle: allocated
+ * (hipMalloc) on the first call that needs it, grown when a later call needs more
+ * (the old one is freed, which waits for work still using it), freed by
+ * gemm_destroy. Calls on one handle that use split-K share that workspace, so they
+ * must be ordered (one stream, or synchronized between streams). The partial sums
+ * are added in a fixed order, so results are reproducible run to run. */
 gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                        const void* B, int64_t ldb, void* C, int64_t ldc, gemm_dtype_t dtype, void* stream);
 
-/* Release a handle. NULL or an already destroyed handle -> GEMM_ERR_INVALID_ARG. */
+/* Release a handle and its split-K workspace (hipFree waits for work still using it).
+ * NULL or an already destroyed handle -> GEMM_ERR_INVALID_ARG. */
 gemm_status_t gemm_destroy(gemm_handle_t h);
 
 /* Force the C tile (tm x tn) and K-step tk of later gemm_run calls on this handle;
@@ -111,6 +122,16 @@ gemm_status_t gemm_destroy(gemm_handle_t h);
  * is checked by gemm_run/gemm_plan (GEMM_ERR_UNSUPPORTED_TILE). Negative values or
  * a partial zero triple -> GEMM_ERR_INVALID_ARG. */
 gemm_status_t gemm_set_tile(gemm_handle_t h, int32_t tm, int32_t tn, int32_t tk);
+
+/* Force the number of K-slices S of later gemm_run calls on this handle that use
+ * the macro-tile MFMA kernel (gemm_plan_t.kernel == 4); other kernels ignore it.
+ * 0 returns to the library's choice (split only with automatic tiles, when the C
+ * tiles cannot fill half of the GPU and K is long), 1 never splits, 2..64 ask for
+ * S slices: each holds cdiv(nk, S) of the nk K-tiles, and S is lowered so that no
+ * slice is empty (gemm_plan reports the count used). Split-K needs a workspace of
+ * S * M * N * 4 bytes (see gemm_run). Out of range or a bad handle ->
+ * GEMM_ERR_INVALID_ARG. */
+gemm_status_t gemm_set_split_k(gemm_handle_t h, int32_t splits);
 
 /* Validate gemm_run's arguments without a handle and without any HIP call.
  * Returns exactly the status gemm_run would return for an argument error, or

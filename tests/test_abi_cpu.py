@@ -86,6 +86,7 @@ def test_null_pointers_allowed_for_empty_matrices():
 def test_null_or_unknown_handle():
     assert tgemm.gemm_destroy(None) == tgemm.ERR_INVALID_ARG
     assert tgemm.gemm_set_tile(None, 16, 16, 32) == tgemm.ERR_INVALID_ARG
+    assert tgemm.gemm_set_split_k(None, 2) == tgemm.ERR_INVALID_ARG
     assert tgemm.gemm_run(None, *ok_args(), tgemm.BF16_BF16, None) == tgemm.ERR_INVALID_ARG
     bogus = ctypes.c_void_p(0xDEADBEEF0)
     assert tgemm.gemm_destroy(bogus) == tgemm.ERR_INVALID_ARG
@@ -118,6 +119,23 @@ def test_plan_auto_tiles():
     assert p["kernel_name"] == "mfma_macro_tile" and p["vector_loads"] == 1
     p = plan(9, 9, 9, tgemm.I32_I32)
     assert p["kernel_name"] == "int32_valu"
+
+
+def test_plan_split_k():
+    # few C tiles and a long K: the reduction is cut into K-slices
+    p = plan(128, 8192, 8192, tgemm.BF16_BF16)
+    assert (p["tile_m"], p["tile_n"], p["grid"]) == (128, 128, 64)
+    assert p["split_k"] == 4  # 256 workgroups: one per compute unit
+    p = plan(64, 64, 4096, tgemm.BF16_F32)   # one 64x64 tile, 64 K-tiles -> 16 slices of 4
+    assert p["grid"] == 1 and p["split_k"] == 16
+    p = plan(64, 64, 448, tgemm.F16_F16)     # 7 K-tiles: too short to split
+    assert p["split_k"] == 1
+    p = plan(96, 96, 2000, tgemm.BF16_F32)   # four 64x64 tiles, 32 K-tiles (ragged) -> 8 slices of 4
+    assert p["split_k"] == 8
+    # enough tiles, the integer path, empty products: no split
+    for args in ((8192, 8192, 8192, tgemm.BF16_BF16), (4096, 4096, 4096, tgemm.BF16_BF16),
+                 (9, 9, 9000, tgemm.I32_I32), (0, 64, 4096, tgemm.BF16_F32), (64, 64, 0, tgemm.BF16_F32)):
+        assert plan(*args)["split_k"] == 1, args
 
 
 def test_plan_vector_loads_need_alignment():

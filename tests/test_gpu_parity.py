@@ -42,12 +42,14 @@ def oracle_ref(o, a, b, dtype):
     return o.gemm(a, b, G.IN_KIND[dtype], G.OUT_KIND[dtype])
 
 
-def check_full(h, o, a, b, dtype, tile=None, **layout):
+def check_full(h, o, a, b, dtype, tile=None, splits=0, **layout):
     set_tile(h, tile)
+    tgemm.check(tgemm.gemm_set_split_k(h, splits), "gemm_set_split_k")
     try:
         c, dc = G.run(h, a, b, dtype, **layout)
     finally:
         set_tile(h, None)
+        tgemm.gemm_set_split_k(h, 0)
     assert dc.untouched_outside(), "kernel wrote outside C"
     ref = oracle_ref(o, a, b, dtype)
     if dtype == tgemm.I32_I32:
@@ -248,3 +250,85 @@ def test_repeatable_and_side_stream(h, o):
         c2, _ = G.run(h, a, b, tgemm.BF16_F32, stream=s)
     assert np.array_equal(c1, c2)
     G.compare(c1, oracle_ref(o, a, b, tgemm.BF16_F32).view(np.int32), "f32")
+
+
+# ---------------------------------------------------------------- split-K
+
+def plan_of(h, M, N, K, dtype, splits=0, tile=None):
+    """gemm_plan for dense row-major operands under a forced split count / tile."""
+    set_tile(h, tile)
+    tgemm.check(tgemm.gemm_set_split_k(h, splits), "gemm_set_split_k")
+    try:
+        return tgemm.gemm_plan(h, M, N, K, 1 << 20, K, 1 << 21, N, 1 << 22, N, dtype)
+    finally:
+        set_tile(h, None)
+        tgemm.gemm_set_split_k(h, 0)
+
+
+SPLIT_SHAPES = [(200, 136, 1000), (130, 70, 777), (256, 256, 4096), (64, 512, 640), (1, 8, 2048)]
+
+
+@pytest.mark.parametrize("splits", [2, 3, 5, 16, 64])
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=str)
+def test_split_k_forced(h, o, shape, splits):
+    """K cut into slices (ragged last slice, ragged K tail, element and direct
+    loaders), fp32 partial tiles summed in slice order, one rounding at the end."""
+    M, N, K = shape
+    nk = -(-K // 64)
+    for n, dtype in enumerate([tgemm.BF16_BF16, tgemm.F16_F32, tgemm.BF16_F32, tgemm.F16_F16]):
+        p = plan_of(h, M, N, K, dtype, splits)
+        assert p["kernel_name"] == "mfma_macro_tile"
+        per = -(-nk // min(splits, nk))
+        assert p["split_k"] == -(-nk // per) and p["split_k"] <= splits
+        a, b = inputs.random_case(M, N, K, G.IN_KIND[dtype], seed=31 * splits + n)
+        check_full(h, o, a, b, dtype, splits=splits)
+
+
+@pytest.mark.parametrize("splits", [0, 4, 7])
+def test_split_k_integer_inputs_bit_exact(h, o, splits):
+    """Integer-valued inputs: every partial sum is exact, so the split result must
+    equal the oracle bit for bit, whatever the slicing."""
+    for M, N, K in [(96, 200, 3000), (128, 8192 // 8, 4096), (33, 40, 1100)]:
+        for dtype, kind in [(tgemm.BF16_F32, "bf16"), (tgemm.F16_F16, "f16")]:
+            a = inputs.draw((M, K), "small_int", kind, 41 + M)
+            b = inputs.draw((K, N), "small_int", kind, 43 + N)
+            tgemm.check(tgemm.gemm_set_split_k(h, splits))
+            try:
+                c, dc = G.run(h, a, b, dtype)
+            finally:
+                tgemm.gemm_set_split_k(h, 0)
+            assert dc.untouched_outside()
+            ref = oracle_ref(o, a, b, dtype).view(G.np_int(tgemm.OUT_BYTES[dtype]))
+            assert np.array_equal(c, ref), (M, N, K, dtype, splits)
+
+
+def test_split_k_deterministic_and_workspace_reuse(h, o):
+    """Automatic split: identical bits on repeated calls; the handle's workspace
+    grows for a larger product and is reused by a smaller one."""
+    small = inputs.random_case(64, 128, 2048, "bf16", seed=51)
+    large = inputs.random_case(128, 1024, 4096, "bf16", seed=52)
+    assert plan_of(h, 64, 128, 2048, tgemm.BF16_F32)["split_k"] > 1
+    assert plan_of(h, 128, 1024, 4096, tgemm.BF16_F32)["split_k"] > 1
+    outs = []
+    for a, b in [small, large, small, large]:
+        c, _ = G.run(h, a, b, tgemm.BF16_F32)
+        outs.append(c)
+    assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[1], outs[3])
+    for (a, b), c in zip([small, large], outs[:2]):
+        G.compare(c, oracle_ref(o, a, b, tgemm.BF16_F32).view(np.int32), "f32")
+
+
+def test_split_k_setting_limits(h, o):
+    assert tgemm.gemm_set_split_k(h, -1) == tgemm.ERR_INVALID_ARG
+    assert tgemm.gemm_set_split_k(h, 65) == tgemm.ERR_INVALID_ARG
+    # more slices than K-tiles: lowered to one slice per K-tile
+    assert plan_of(h, 64, 64, 100, tgemm.BF16_F32, splits=64)["split_k"] == 2
+    # 1 turns the automatic split off; other kernels ignore the setting
+    assert plan_of(h, 128, 8192, 8192, tgemm.BF16_BF16, splits=1)["split_k"] == 1
+    assert plan_of(h, 64, 64, 4096, tgemm.BF16_F32, splits=8, tile=(16, 16, 32))["split_k"] == 1
+    assert plan_of(h, 64, 64, 4096, tgemm.I32_I32, splits=8)["split_k"] == 1
+    a, b = inputs.random_case(64, 64, 4096, "bf16", seed=61)
+    check_full(h, o, a, b, tgemm.BF16_F32, tile=(16, 16, 32), splits=8)
+    check_full(h, o, a, b, tgemm.BF16_F32, splits=1)
+    # a forced tile with a forced split
+    check_full(h, o, a, b, tgemm.BF16_BF16, tile=(128, 128, 64), splits=6)

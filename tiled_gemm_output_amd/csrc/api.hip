@@ -16,7 +16,10 @@
 struct tgemm_handle {
   int device;
   int cus;
-  int tm, tn, tk;  // forced tile, 0 = automatic
+  int tm, tn, tk;   // forced tile, 0 = automatic
+  int splits;       // forced K-slice count, 0 = automatic
+  void* ws;         // split-K workspace (device memory owned by the handle), or null
+  size_t ws_bytes;  // its size
 };
 
 namespace {
@@ -32,6 +35,7 @@ bool is_live(const tgemm_handle* h) {
 }
 
 constexpr int64_t kI32Max = 0x7fffffffLL;
+constexpr int kMaxSplits = 64;  // largest K-slice count gemm_set_split_k accepts
 constexpr int64_t kMaxRecords = 0x7FFFFFF0LL;  // must match device_common.h
 
 int out_bytes(int dtype) { return (dtype == GEMM_I32_I32 || dtype == GEMM_F16_F32 || dtype == GEMM_BF16_F32) ? 4 : 2; }
@@ -120,6 +124,7 @@ gemm_status_t plan_impl(const tgemm_handle* h, int64_t M, int64_t N, int64_t K, 
     }
     p.vector_loads = vector_ok(N, K, A, lda, B, ldb, p.tile_m, p.tile_n, p.tile_k) ? 1 : 0;
   }
+  p.split_k = 1;
   if (M == 0 || N == 0) {
     p.kernel = 0;
     p.grid = 0;
@@ -129,6 +134,25 @@ gemm_status_t plan_impl(const tgemm_handle* h, int64_t M, int64_t N, int64_t K, 
   } else {
     p.grid = cdiv(M, p.tile_m) * cdiv(N, p.tile_n);
     if (p.grid > kI32Max) return GEMM_ERR_INVALID_ARG;
+    // Split-K (automatic tiles only): when the C tiles cannot fill half of the chip
+    // and the reduction is long, each tile's K range is cut into slices computed by
+    // separate workgroups; their fp32 partial tiles are summed by a second kernel.
+    // A forced slice count (gemm_set_split_k) replaces the heuristic. Slices hold
+    // cdiv(nk, S) K-tiles each, and S is lowered so that none is empty.
+    const int64_t nk = cdiv(K, p.tile_k);
+    const int fs = h ? h->splits : 0;
+    int64_t sk = 1;
+    if (p.kernel == 4) {
+      if (fs > 0) {
+        sk = fs;
+      } else if (!forced && p.grid < 128 && nk >= 8) {
+        sk = 256 / p.grid;
+        if (sk > 16) sk = 16;
+        if (sk > nk / 4) sk = nk / 4;
+      }
+    }
+    if (sk > nk) sk = nk;
+    if (sk >= 2) p.split_k = (int32_t)cdiv(nk, cdiv(nk, sk));
   }
   *out = p;
   return GEMM_OK;
@@ -184,6 +208,9 @@ gemm_status_t gemm_create(gemm_handle_t* out) {
   h->device = dev;
   h->cus = prop.multiProcessorCount;
   h->tm = h->tn = h->tk = 0;
+  h->splits = 0;
+  h->ws = nullptr;
+  h->ws_bytes = 0;
   {
     std::lock_guard<std::mutex> g(g_mu);
     live().insert(h);
@@ -197,8 +224,10 @@ gemm_status_t gemm_destroy(gemm_handle_t h) {
     std::lock_guard<std::mutex> g(g_mu);
     if (h == nullptr || live().erase(h) == 0) return GEMM_ERR_INVALID_ARG;
   }
+  gemm_status_t st = GEMM_OK;
+  if (h->ws != nullptr && hipFree(h->ws) != hipSuccess) st = GEMM_ERR_HIP;  // waits for work using it
   delete h;
-  return GEMM_OK;
+  return st;
 }
 
 gemm_status_t gemm_set_tile(gemm_handle_t h, int32_t tm, int32_t tn, int32_t tk) {
@@ -208,6 +237,13 @@ gemm_status_t gemm_set_tile(gemm_handle_t h, int32_t tm, int32_t tn, int32_t tk)
   h->tm = tm;
   h->tn = tn;
   h->tk = tk;
+  return GEMM_OK;
+}
+
+gemm_status_t gemm_set_split_k(gemm_handle_t h, int32_t splits) {
+  if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
+  if (splits < 0 || splits > kMaxSplits) return GEMM_ERR_INVALID_ARG;
+  h->splits = splits;
   return GEMM_OK;
 }
 
@@ -254,6 +290,23 @@ gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const v
       break;
     }
     default: {
+      const int splits = p.split_k > 1 ? p.split_k : 1;
+      if (splits > 1) {
+        const size_t need = (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+        if (h->ws_bytes < need) {
+          if (h->ws != nullptr) {
+            if (hipFree(h->ws) != hipSuccess) return GEMM_ERR_HIP;
+            h->ws = nullptr;
+            h->ws_bytes = 0;
+          }
+          if (hipMalloc(&h->ws, need) != hipSuccess) {
+            (void)hipGetLastError();
+            h->ws = nullptr;
+            return GEMM_ERR_OUT_OF_MEMORY;
+          }
+          h->ws_bytes = need;
+        }
+      }
       tg::MacroArgs a;
       a.A = (const uint16_t*)A;
       a.B = (const uint16_t*)B;
@@ -266,12 +319,25 @@ gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const v
       a.ldc = ldc;
       a.tiles_m = (int)cdiv(M, p.tile_m);
       a.tiles_n = (int)cdiv(N, p.tile_n);
-      a.group_m = a.tiles_m < 8 ? a.tiles_m : 8;
-      if (p.kernel == 3)
+      a.group_m = a.tiles_m < 4 ? a.tiles_m : 4;
+      const int64_t nk = cdiv(K, p.tile_k);
+      a.kt_per_split = (int)cdiv(nk, splits);
+      a.split_stride = (int64_t)M * N;
+      if (p.kernel == 3) {
         e = tg::launch_small(a, in_kind(dtype), out_kind(dtype), p.vector_loads != 0, s, p.grid);
-      else
+      } else if (splits == 1) {
         e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k), a, in_kind(dtype), out_kind(dtype),
-                             p.vector_loads != 0, s, p.grid);
+                             p.vector_loads != 0, s, p.grid, 1);
+      } else {
+        // partial tiles (fp32, dense, ldc = N) into the workspace, then the ordered reduction
+        tg::MacroArgs w = a;
+        w.C = h->ws;
+        w.ldc = N;
+        e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k), w, in_kind(dtype), 0, p.vector_loads != 0, s,
+                             p.grid, splits);
+        if (e == hipSuccess)
+          e = tg::launch_splitk_reduce((const float*)h->ws, splits, C, ldc, (int)M, (int)N, out_kind(dtype), s);
+      }
       break;
     }
   }

@@ -14,6 +14,11 @@ struct MacroArgs {
   int M, N, K;
   int64_t lda, ldb, ldc;
   int tiles_m, tiles_n, group_m;
+  // split-K: workgroup (tile, blockIdx.y) reduces K-tiles [y * kt_per_split, (y+1) * kt_per_split)
+  // and writes its fp32 partial tile at C + y * split_stride (elements); without split-K,
+  // kt_per_split covers all K-tiles and gridDim.y == 1
+  int kt_per_split;
+  int64_t split_stride;
 };
 
 struct MacroShape {
@@ -23,7 +28,11 @@ constexpr int kNumMacroShapes = 5;
 extern const MacroShape kMacroShapes[kNumMacroShapes];
 
 // in: 0 = f16, 1 = bf16. out: 0 = f32, 1 = bf16, 2 = f16.
-hipError_t launch_macro(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid);
+hipError_t launch_macro(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
+                        int splits);
+// C[0:M, 0:N] = sum over s < splits of ws[s][M][N] (dense fp32 partials, summed in slice order),
+// rounded to the output format (out: 0 = f32, 1 = bf16, 2 = f16).
+hipError_t launch_splitk_reduce(const float* ws, int splits, void* C, int64_t ldc, int M, int N, int out, hipStream_t s);
 hipError_t launch_small(const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid);
 
 struct I32Args {

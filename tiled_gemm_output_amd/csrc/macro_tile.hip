@@ -132,7 +132,10 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   const int row0 = tile_m * BM, col0 = tile_n * BN;
   const int M = p.M, N = p.N, K = p.K;
   const int64_t lda = p.lda, ldb = p.ldb;
-  const int nk = (K + BK - 1) / BK;
+  // K-tiles of this workgroup: [kt_base, kt_base + nk) (all of them without split-K)
+  const int kt_base = blockIdx.y * p.kt_per_split;
+  const int nk_all = (K + BK - 1) / BK;
+  const int nk = (nk_all - kt_base) < p.kt_per_split ? (nk_all - kt_base) : p.kt_per_split;
 
   // ---------------- loader geometry ----------------
   // Block t of a wave fills 1 KiB of a stage. A: 8 rows of 128 bytes per block;
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   // load writes exact, so it adds no waits before reads of the other stage).
   auto issue_loads = [&](TG_LDS char* sa, TG_LDS char* sb, int kt) {
     const bool ok = (unsigned)kt < (unsigned)nk;
-    const int k0 = ok ? kt * BK : 0;
+    const int k0 = ok ? (kt_base + kt) * BK : 0;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(gA + k0, ok ? ((int64_t)(M - 1 - row0) * lda + (K - k0)) * 2 : 0);
     const __amdgpu_buffer_rsrc_t rb =
         make_rsrc(gB + (int64_t)k0 * ldb, ok ? ((int64_t)(K - 1 - k0) * ldb + (N - col0)) * 2 : 0);
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   i32x4 a_reg[kAPer], b_reg[kBPer];
   auto fetch_regs = [&](int kt) {
     const bool ok = (unsigned)kt < (unsigned)nk;
-    const int k0 = kt * BK;
+    const int k0 = (kt_base + kt) * BK;
 #pragma unroll
     for (int t = 0; t < kAPer; ++t) {
       const int r = a_row(t, lane);
@@ -363,6 +366,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   // of the wave tile. Interior tiles store without bounds checks; edge tiles drop
   // the elements outside C.
   const int64_t ldc = p.ldc;
+  char* const Cout = (char*)p.C + (int64_t)blockIdx.y * p.split_stride * (OUT == OUT_F32 ? 4 : 2);
   const bool interior = row0 + BM <= M && col0 + BN <= N;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -378,23 +382,87 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
           const int64_t off = base + (int64_t)dr * ldc;
           const float x = acc[i][j][v];
           if constexpr (OUT == OUT_F32)
-            ((float*)p.C)[off] = x;
+            ((float*)Cout)[off] = x;
           else if constexpr (OUT == OUT_BF16)
-            ((uint16_t*)p.C)[off] = f32_to_bf16_rne(x);
+            ((uint16_t*)Cout)[off] = f32_to_bf16_rne(x);
           else
-            ((uint16_t*)p.C)[off] = f32_to_f16_rne(x);
+            ((uint16_t*)Cout)[off] = f32_to_f16_rne(x);
         }
       }
     }
   }
 }
 
+// Split-K reduction: the partial tiles of the K-slices are summed in slice order
+// (deterministic) and rounded once to the output format.
+template <int OUT>
+__device__ __forceinline__ void store_out(void* C, int64_t off, float x) {
+  if constexpr (OUT == OUT_F32)
+    ((float*)C)[off] = x;
+  else if constexpr (OUT == OUT_BF16)
+    ((uint16_t*)C)[off] = f32_to_bf16_rne(x);
+  else
+    ((uint16_t*)C)[off] = f32_to_f16_rne(x);
+}
+
+// Each thread sums G consecutive elements of one row (G = 4 when N % 4 == 0: the
+// workspace is dense, so every group is a 16-byte aligned vector of one row).
+template <int OUT, int G>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* ws, int splits, void* C, int64_t ldc, int M,
+                                                           int N) {
+  const int64_t slice = (int64_t)M * N, groups = slice / G;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < groups; q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = q * G, r = e / N, c = e - r * N;
+    if constexpr (G == 4) {
+      f32x4 acc = *(const f32x4*)(ws + e);
+      for (int s = 1; s < splits; ++s) {
+        const f32x4 x = *(const f32x4*)(ws + s * slice + e);
+        acc.x += x.x;
+        acc.y += x.y;
+        acc.z += x.z;
+        acc.w += x.w;
+      }
+      store_out<OUT>(C, r * ldc + c, acc.x);
+      store_out<OUT>(C, r * ldc + c + 1, acc.y);
+      store_out<OUT>(C, r * ldc + c + 2, acc.z);
+      store_out<OUT>(C, r * ldc + c + 3, acc.w);
+    } else {
+      float acc = ws[e];
+      for (int s = 1; s < splits; ++s) acc += ws[s * slice + e];
+      store_out<OUT>(C, r * ldc + c, acc);
+    }
+  }
+}
+
+template <int OUT>
+static void launch_reduce(const float* ws, int splits, void* C, int64_t ldc, int M, int N, hipStream_t s) {
+  const bool v4 = N % 4 == 0;
+  const int64_t groups = (int64_t)M * N / (v4 ? 4 : 1);
+  int64_t blocks = (groups + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (v4)
+    hipLaunchKernelGGL((splitk_reduce_kernel<OUT, 4>), dim3((unsigned)blocks), dim3(256), 0, s, ws, splits, C, ldc, M, N);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<OUT, 1>), dim3((unsigned)blocks), dim3(256), 0, s, ws, splits, C, ldc, M, N);
+}
+
+hipError_t launch_splitk_reduce(const float* ws, int splits, void* C, int64_t ldc, int M, int N, int out,
+                                hipStream_t s) {
+  if (out == OUT_F32)
+    launch_reduce<OUT_F32>(ws, splits, C, ldc, M, N, s);
+  else if (out == OUT_BF16)
+    launch_reduce<OUT_BF16>(ws, splits, C, ldc, M, N, s);
+  else
+    launch_reduce<OUT_F16>(ws, splits, C, ldc, M, N, s);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // host-side instantiation and launch
 
 template <class Cfg, int IN, int OUT>
-static hipError_t launch_cfg(const MacroArgs& a, bool vec, hipStream_t stream, int64_t grid) {
-  const dim3 g((unsigned)grid), b(Cfg::kThreads);
+static hipError_t launch_cfg(const MacroArgs& a, bool vec, hipStream_t stream, int64_t grid, int splits) {
+  const dim3 g((unsigned)grid, (unsigned)splits), b(Cfg::kThreads);
   if (!vec)
     hipLaunchKernelGGL((macro_tile_kernel<Cfg, IN, OUT, kLoadElem>), g, b, 0, stream, a);
   else if (a.K % Cfg::BK == 0)
@@ -405,11 +473,12 @@ static hipError_t launch_cfg(const MacroArgs& a, bool vec, hipStream_t stream, i
 }
 
 template <class Cfg>
-static hipError_t launch_dtype(const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid) {
-  if (in == IN_BF16 && out == OUT_F32) return launch_cfg<Cfg, IN_BF16, OUT_F32>(a, vec, s, grid);
-  if (in == IN_BF16 && out == OUT_BF16) return launch_cfg<Cfg, IN_BF16, OUT_BF16>(a, vec, s, grid);
-  if (in == IN_F16 && out == OUT_F32) return launch_cfg<Cfg, IN_F16, OUT_F32>(a, vec, s, grid);
-  if (in == IN_F16 && out == OUT_F16) return launch_cfg<Cfg, IN_F16, OUT_F16>(a, vec, s, grid);
+static hipError_t launch_dtype(const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
+                               int splits) {
+  if (in == IN_BF16 && out == OUT_F32) return launch_cfg<Cfg, IN_BF16, OUT_F32>(a, vec, s, grid, splits);
+  if (in == IN_BF16 && out == OUT_BF16) return launch_cfg<Cfg, IN_BF16, OUT_BF16>(a, vec, s, grid, splits);
+  if (in == IN_F16 && out == OUT_F32) return launch_cfg<Cfg, IN_F16, OUT_F32>(a, vec, s, grid, splits);
+  if (in == IN_F16 && out == OUT_F16) return launch_cfg<Cfg, IN_F16, OUT_F16>(a, vec, s, grid, splits);
   return hipErrorInvalidValue;
 }
 
@@ -427,13 +496,14 @@ const MacroShape kMacroShapes[kNumMacroShapes] = {
     {256, 256, 64, Cfg256x256w4::kThreads, Cfg256x256w4::kLds},
 };
 
-hipError_t launch_macro(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid) {
+hipError_t launch_macro(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
+                        int splits) {
   switch (shape) {
-    case 0: return launch_dtype<Cfg256x256w8>(a, in, out, vec, s, grid);
-    case 1: return launch_dtype<Cfg256x128>(a, in, out, vec, s, grid);
-    case 2: return launch_dtype<Cfg128x128>(a, in, out, vec, s, grid);
-    case 3: return launch_dtype<Cfg64x64>(a, in, out, vec, s, grid);
-    case 4: return launch_dtype<Cfg256x256w4>(a, in, out, vec, s, grid);
+    case 0: return launch_dtype<Cfg256x256w8>(a, in, out, vec, s, grid, splits);
+    case 1: return launch_dtype<Cfg256x128>(a, in, out, vec, s, grid, splits);
+    case 2: return launch_dtype<Cfg128x128>(a, in, out, vec, s, grid, splits);
+    case 3: return launch_dtype<Cfg64x64>(a, in, out, vec, s, grid, splits);
+    case 4: return launch_dtype<Cfg256x256w4>(a, in, out, vec, s, grid, splits);
     default: return hipErrorInvalidValue;
   }
 }

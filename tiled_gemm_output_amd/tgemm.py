@@ -26,17 +26,17 @@ IN_BYTES = {I32_I32: 4, F16_F32: 2, BF16_F32: 2, BF16_BF16: 2, F16_F16: 2}
 OUT_BYTES = {I32_I32: 4, F16_F32: 4, BF16_F32: 4, BF16_BF16: 2, F16_F16: 2}
 KERNEL_NAMES = {0: "none", 1: "zero_fill", 2: "int32_valu", 3: "mfma_16x16x32_one_wave", 4: "mfma_macro_tile"}
 
-EXPORTS = ["gemm_create", "gemm_run", "gemm_destroy", "gemm_set_tile", "gemm_check_args", "gemm_plan",
-           "gemm_status_string"]
+EXPORTS = ["gemm_create", "gemm_run", "gemm_destroy", "gemm_set_tile", "gemm_set_split_k", "gemm_check_args",
+           "gemm_plan", "gemm_status_string"]
 
 
 class GemmPlan(ctypes.Structure):
     _fields_ = [("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("vector_loads", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int32), ("split_k", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
-        d = {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        d = {name: getattr(self, name) for name, _ in self._fields_}
         d["kernel_name"] = KERNEL_NAMES.get(self.kernel, "?")
         return d
 
@@ -67,6 +67,8 @@ def load(path: str = LIBRARY):
     lib.gemm_destroy.restype = i32
     lib.gemm_set_tile.argtypes = [vp, i32, i32, i32]
     lib.gemm_set_tile.restype = i32
+    lib.gemm_set_split_k.argtypes = [vp, i32]
+    lib.gemm_set_split_k.restype = i32
     lib.gemm_check_args.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32]
     lib.gemm_check_args.restype = i32
     lib.gemm_plan.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, ctypes.POINTER(GemmPlan)]
@@ -99,6 +101,10 @@ def gemm_destroy(h) -> int:
 
 def gemm_set_tile(h, tm: int, tn: int, tk: int) -> int:
     return load().gemm_set_tile(h, tm, tn, tk)
+
+
+def gemm_set_split_k(h, splits: int) -> int:
+    return load().gemm_set_split_k(h, splits)
 
 
 def gemm_run(h, M, N, K, A, lda, B, ldb, C, ldc, dtype, stream=None) -> int:
@@ -150,6 +156,9 @@ class Gemm:
 
     def set_tile(self, tm: int, tn: int, tk: int) -> None:
         check(gemm_set_tile(self.h, tm, tn, tk), "gemm_set_tile")
+
+    def set_split_k(self, splits: int) -> None:
+        check(gemm_set_split_k(self.h, splits), "gemm_set_split_k")
 
     def plan(self, a, b, c, dtype) -> dict:
         return gemm_plan(self.h, *tensor_args(a, b, c), dtype)
