@@ -110,6 +110,8 @@ def main() -> int:
     ap.add_argument("--workload", default="square8192_bf16")
     ap.add_argument("--tile", default=None, help="force a tile, e.g. 256,256,64")
     ap.add_argument("--split-k", type=int, default=0, help="force the K-slice count (0: the library's choice)")
+    ap.add_argument("--op", default="nn", choices=["nn", "nt", "tn", "tt"],
+                    help="operand forms: t = that operand is stored transposed (A as K x M, B as N x K)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -147,21 +149,28 @@ def main() -> int:
     dtype = tgemm.DTYPES[w.dtype]
     log("bench: workload %s M=%d N=%d K=%d dtype=%s" % (w.name, w.M, w.N, w.K, w.dtype))
     a, b = inputs.make(w)
-    da = torch.from_numpy(a.view(np.int16 if a.dtype == np.uint16 else np.int32)).cuda()
-    db = torch.from_numpy(b.view(np.int16 if b.dtype == np.uint16 else np.int32)).cuda()
+    op_a = tgemm.OP_T if args.op[0] == "t" else tgemm.OP_N
+    op_b = tgemm.OP_T if args.op[1] == "t" else tgemm.OP_N
+    sa = np.ascontiguousarray(a.T) if op_a == tgemm.OP_T else a  # what is stored on the device
+    sb = np.ascontiguousarray(b.T) if op_b == tgemm.OP_T else b
+    lda, ldb = sa.shape[1], sb.shape[1]
+    da = torch.from_numpy(sa.view(np.int16 if a.dtype == np.uint16 else np.int32)).cuda()
+    db = torch.from_numpy(sb.view(np.int16 if b.dtype == np.uint16 else np.int32)).cuda()
+    del sa, sb
     ob = tgemm.OUT_BYTES[dtype]
     dc = torch.empty((w.M, w.N), dtype=torch.int16 if ob == 2 else torch.int32, device="cuda")
     h = tgemm.gemm_create()
     if args.tile:
         tgemm.check(tgemm.gemm_set_tile(h, *[int(x) for x in args.tile.split(",")]))
     tgemm.check(tgemm.gemm_set_split_k(h, args.split_k), "gemm_set_split_k")
-    plan = tgemm.gemm_plan(h, w.M, w.N, w.K, da.data_ptr(), w.K, db.data_ptr(), w.N, dc.data_ptr(), w.N, dtype)
+    plan = tgemm.gemm_plan_op(h, op_a, op_b, w.M, w.N, w.K, da.data_ptr(), lda, db.data_ptr(), ldb, dc.data_ptr(),
+                              w.N, dtype)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
     def step():
-        tgemm.check(tgemm.gemm_run(h, w.M, w.N, w.K, da.data_ptr(), w.K, db.data_ptr(), w.N, dc.data_ptr(), w.N,
-                                   dtype, sp), "gemm_run")
+        tgemm.check(tgemm.gemm_run_op(h, op_a, op_b, w.M, w.N, w.K, da.data_ptr(), lda, db.data_ptr(), ldb,
+                                      dc.data_ptr(), w.N, dtype, sp), "gemm_run_op")
 
     for _ in range(args.warmup):
         step()
@@ -192,7 +201,9 @@ def main() -> int:
     compulsory = ib * (w.M * w.K + w.K * w.N) + ob * w.M * w.N
     intensity = flops / compulsory
     sha = kernel_source_sha()
-    traffic = load_traffic(w.name, sha)
+    # the recorded counters are for the default launch (library's tile and split, no transposes)
+    default_launch = args.op == "nn" and not args.tile and args.split_k == 0
+    traffic = load_traffic(w.name, sha) if default_launch else None
     if intensity >= RIDGE:
         achieved = flops / (launch_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_16BIT_TFLOPS, "unit": "TFLOP/s",
@@ -217,7 +228,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.in_kind, "acc": "fp32" if ib == 2 else "i32",
                    "out": w.out_kind, "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
-                   "kernel": plan["kernel_name"], "grid": plan["grid"], "split_k": plan["split_k"],
+                   "op": args.op, "kernel": plan["kernel_name"], "grid": plan["grid"], "split_k": plan["split_k"],
                    "threads": plan["threads"],
                    "vector_loads": plan["vector_loads"], "kernel_source_sha": sha},
         "pct_of_mfma_peak": 100.0 * value / PEAK_MFMA_16BIT_TFLOPS,

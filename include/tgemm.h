@@ -32,7 +32,9 @@
  *  - C must not overlap A or B (not checked).
  *  - Any alignment of A, B, C and any leading dimension >= the row length is
  *    accepted; a slower element-wise loader is used when 16-byte vector loads are
- *    not possible.
+ *    not possible (they need 16-byte aligned A and B, leading dimensions and the
+ *    contiguous extent of each stored operand in multiples of 8 elements).
+ *  - Operands may also be supplied transposed (gemm_run_op).
  *  - A handle may be used by one host thread at a time.
  */
 #ifndef TGEMM_H
@@ -66,6 +68,12 @@ typedef enum {
   GEMM_BF16_BF16 = 3, /* bfloat16 in, fp32 accumulate, bfloat16 out (round to nearest even) */
   GEMM_F16_F16 = 4    /* binary16 in, fp32 accumulate, binary16 out (round to nearest even) */
 } gemm_dtype_t;
+
+/* Operand forms (int32) for the *_op entry points: op(X) = X or X^T. */
+typedef enum {
+  GEMM_OP_N = 0, /* as given: A stored M x K (lda >= K), B stored K x N (ldb >= N) */
+  GEMM_OP_T = 1  /* transposed: A stored K x M (lda >= M), B stored N x K (ldb >= K) */
+} gemm_op_t;
 
 /* The kernel configuration gemm_run would use for a call (see gemm_plan). */
 typedef struct {
@@ -109,6 +117,22 @@ gemm_status_t gemm_create(gemm_handle_t* out);
 gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                        const void* B, int64_t ldb, void* C, int64_t ldc, gemm_dtype_t dtype, void* stream);
 
+/* C = op(A) @ op(B) with either operand supplied transposed (Mojo GPU puzzles,
+ * "Tiled Matrix Multiplication", the section on transposed loading: a transposed
+ * operand is read through the same shared tile). op(A) is M x K and op(B) is K x N
+ * whatever the storage:
+ *   op_a == GEMM_OP_N: op(A)[i][k] = A[i * lda + k], lda >= max(K, 1);
+ *   op_a == GEMM_OP_T: op(A)[i][k] = A[k * lda + i], lda >= max(M, 1) (A stored K x M);
+ *   op_b == GEMM_OP_N: op(B)[k][j] = B[k * ldb + j], ldb >= max(N, 1);
+ *   op_b == GEMM_OP_T: op(B)[k][j] = B[j * ldb + k], ldb >= max(K, 1) (B stored N x K).
+ * C is M x N row-major as in gemm_run. Everything else (dtypes, tiles, split-K,
+ * empty and K == 0 cases, errors, asynchrony) is as gemm_run, which is
+ * gemm_run_op(GEMM_OP_N, GEMM_OP_N, ...). An op other than GEMM_OP_N/GEMM_OP_T ->
+ * GEMM_ERR_INVALID_ARG. */
+gemm_status_t gemm_run_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                          const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                          gemm_dtype_t dtype, void* stream);
+
 /* Release a handle and its split-K workspace (hipFree waits for work still using it).
  * NULL or an already destroyed handle -> GEMM_ERR_INVALID_ARG. */
 gemm_status_t gemm_destroy(gemm_handle_t h);
@@ -139,12 +163,22 @@ gemm_status_t gemm_set_split_k(gemm_handle_t h, int32_t splits);
 gemm_status_t gemm_check_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                               int64_t ldb, const void* C, int64_t ldc, gemm_dtype_t dtype);
 
+/* gemm_check_args for gemm_run_op's arguments (operand forms as gemm_run_op). */
+gemm_status_t gemm_check_args_op(gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K, const void* A,
+                                 int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc,
+                                 gemm_dtype_t dtype);
+
 /* The configuration gemm_run would use for these arguments on this handle
  * (honouring gemm_set_tile). Host-only. h may be NULL (then the automatic
  * choice is reported). Errors as gemm_check_args, plus GEMM_ERR_UNSUPPORTED_TILE. */
 gemm_status_t gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                         const void* B, int64_t ldb, const void* C, int64_t ldc, gemm_dtype_t dtype,
                         gemm_plan_t* out);
+
+/* gemm_plan for gemm_run_op's arguments. */
+gemm_status_t gemm_plan_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                           const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc,
+                           gemm_dtype_t dtype, gemm_plan_t* out);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* gemm_status_string(gemm_status_t s);

@@ -78,21 +78,31 @@ class DevMatrix:
         return bool((self.buf[mask] == self.fill).all().item())
 
 
-def run(h, a: np.ndarray, b: np.ndarray, dtype: int, lda=None, ldb=None, ldc=None, offs=(0, 0, 0), stream=None):
-    """Copy A, B to the device with the given layout, run gemm_run, return (C host bits, C DevMatrix)."""
+def run(h, a: np.ndarray, b: np.ndarray, dtype: int, lda=None, ldb=None, ldc=None, offs=(0, 0, 0), stream=None,
+        op_a=tgemm.OP_N, op_b=tgemm.OP_N):
+    """Copy A, B to the device with the given layout, run gemm_run (gemm_run_op when an
+    operand is to be supplied transposed: then its transpose is what is stored, with
+    row stride lda / ldb), return (C host bits, C DevMatrix). a is the M x K op(A),
+    b the K x N op(B)."""
     torch = _torch()
     M, K = a.shape
     N = b.shape[1]
     ib = 4 if dtype == tgemm.I32_I32 else 2
     ob = tgemm.OUT_BYTES[dtype]
-    lda = K if lda is None else lda
-    ldb = N if ldb is None else ldb
+    sa = np.ascontiguousarray(a.T) if op_a == tgemm.OP_T else a
+    sb = np.ascontiguousarray(b.T) if op_b == tgemm.OP_T else b
+    lda = sa.shape[1] if lda is None else lda
+    ldb = sb.shape[1] if ldb is None else ldb
     ldc = N if ldc is None else ldc
-    da = DevMatrix(a, M, K, lda, offs[0], ib, fill=0)
-    db = DevMatrix(b, K, N, ldb, offs[1], ib, fill=0)
+    da = DevMatrix(sa, sa.shape[0], sa.shape[1], lda, offs[0], ib, fill=0)
+    db = DevMatrix(sb, sb.shape[0], sb.shape[1], ldb, offs[1], ib, fill=0)
     dc = DevMatrix(None, M, N, ldc, offs[2], ob)
     s = stream if stream is not None else torch.cuda.current_stream()
-    st = tgemm.gemm_run(h, M, N, K, da.ptr, da.ld, db.ptr, db.ld, dc.ptr, dc.ld, dtype, s.cuda_stream)
+    if op_a == tgemm.OP_N and op_b == tgemm.OP_N:
+        st = tgemm.gemm_run(h, M, N, K, da.ptr, da.ld, db.ptr, db.ld, dc.ptr, dc.ld, dtype, s.cuda_stream)
+    else:
+        st = tgemm.gemm_run_op(h, op_a, op_b, M, N, K, da.ptr, da.ld, db.ptr, db.ld, dc.ptr, dc.ld, dtype,
+                               s.cuda_stream)
     tgemm.check(st, "gemm_run")
     torch.cuda.synchronize()
     return dc.host(), dc

@@ -70,6 +70,30 @@ def test_bad_args(patch, expected):
     assert tgemm.gemm_check_args(*args, tgemm.BF16_BF16) == expected
 
 
+def test_transposed_operand_strides():
+    """gemm_check_args_op: a transposed A is stored K x M (lda >= M), a transposed B
+    N x K (ldb >= K); op values other than N/T are invalid."""
+    M, N, K = 64, 48, 32
+    ck = tgemm.gemm_check_args_op
+    for op_a in (tgemm.OP_N, tgemm.OP_T):
+        for op_b in (tgemm.OP_N, tgemm.OP_T):
+            lda = M if op_a == tgemm.OP_T else K
+            ldb = K if op_b == tgemm.OP_T else N
+            assert ck(op_a, op_b, M, N, K, NN, lda, NN, ldb, NN, N, tgemm.BF16_F32) == tgemm.OK
+            assert ck(op_a, op_b, M, N, K, NN, lda - 1, NN, ldb, NN, N, tgemm.BF16_F32) == tgemm.ERR_INVALID_ARG
+            assert ck(op_a, op_b, M, N, K, NN, lda, NN, ldb - 1, NN, N, tgemm.BF16_F32) == tgemm.ERR_INVALID_ARG
+    # lda = K = 32 < M = 64 is too short for a transposed A; fine untransposed
+    assert ck(tgemm.OP_T, tgemm.OP_N, M, N, K, NN, K, NN, N, NN, N, tgemm.BF16_F32) == tgemm.ERR_INVALID_ARG
+    assert ck(tgemm.OP_N, tgemm.OP_N, M, N, K, NN, K, NN, N, NN, N, tgemm.BF16_F32) == tgemm.OK
+    for bad in (2, -1):
+        assert ck(bad, tgemm.OP_N, M, N, K, NN, K, NN, N, NN, N, tgemm.BF16_F32) == tgemm.ERR_INVALID_ARG
+        assert ck(tgemm.OP_N, bad, M, N, K, NN, K, NN, N, NN, N, tgemm.BF16_F32) == tgemm.ERR_INVALID_ARG
+    assert tgemm.gemm_run_op(None, tgemm.OP_T, tgemm.OP_N, M, N, K, NN, M, NN, N, NN, N, tgemm.BF16_F32,
+                             None) == tgemm.ERR_INVALID_ARG
+    # gemm_check_args is the (N, N) case
+    assert tgemm.gemm_check_args(*ok_args(), tgemm.BF16_F32) == ck(tgemm.OP_N, tgemm.OP_N, *ok_args(), tgemm.BF16_F32)
+
+
 def test_unknown_dtype():
     assert tgemm.gemm_check_args(*ok_args(), 5) == tgemm.ERR_UNSUPPORTED_DTYPE
     assert tgemm.gemm_check_args(*ok_args(), -1) == tgemm.ERR_UNSUPPORTED_DTYPE
@@ -143,6 +167,33 @@ def test_plan_vector_loads_need_alignment():
     assert plan(256, 256, 256, tgemm.BF16_F32, A=0x10002)["vector_loads"] == 0  # A not 16-byte aligned
     assert plan(256, 256, 256, tgemm.BF16_F32, lda=260)["vector_loads"] == 0    # lda not a multiple of 8
     assert plan(256, 256, 256, tgemm.BF16_F32, lda=264)["vector_loads"] == 1
+
+
+def plan_op(op_a, op_b, M, N, K, dtype, A=0x10000, lda=None, B=0x20000, ldb=None):
+    lda = (M if op_a == tgemm.OP_T else K) if lda is None else lda
+    ldb = (K if op_b == tgemm.OP_T else N) if ldb is None else ldb
+    return tgemm.gemm_plan_op(None, op_a, op_b, M, N, K, ctypes.c_void_p(A), max(lda, 1), ctypes.c_void_p(B),
+                              max(ldb, 1), ctypes.c_void_p(0x30000), max(N, 1), dtype)
+
+
+def test_plan_transposed_vector_loads():
+    """16-byte loads need the contiguous extent of each stored operand in whole
+    8-element chunks: K for A and M for a transposed A; N for B and K for a
+    transposed B."""
+    T, Nn = tgemm.OP_T, tgemm.OP_N
+    assert plan_op(Nn, T, 8192, 8192, 8192, tgemm.BF16_BF16)["vector_loads"] == 1
+    assert plan_op(T, T, 256, 256, 256, tgemm.BF16_F32)["vector_loads"] == 1
+    assert plan_op(T, Nn, 100, 256, 256, tgemm.BF16_F32)["vector_loads"] == 0  # M % 8 != 0, A transposed
+    assert plan_op(Nn, Nn, 100, 256, 256, tgemm.BF16_F32)["vector_loads"] == 1  # M is not contiguous here
+    assert plan_op(Nn, T, 256, 100, 256, tgemm.BF16_F32)["vector_loads"] == 1   # N % 8 != 0 only matters for B as given
+    assert plan_op(Nn, Nn, 256, 100, 256, tgemm.BF16_F32)["vector_loads"] == 0
+    assert plan_op(Nn, T, 256, 256, 100, tgemm.BF16_F32)["vector_loads"] == 0   # K % 8 != 0, B transposed
+    assert plan_op(T, Nn, 256, 256, 100, tgemm.BF16_F32)["vector_loads"] == 1
+    # same tile and split choice as the untransposed product
+    for op_a in (Nn, T):
+        for op_b in (Nn, T):
+            p = plan_op(op_a, op_b, 128, 8192, 8192, tgemm.BF16_F32)
+            assert (p["tile_m"], p["tile_n"], p["split_k"]) == (128, 128, 4)
 
 
 def test_plan_empty_and_zero_k():

@@ -49,13 +49,19 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t max1(int64_t x) { return x > 1 ? x : 1; }
 
 // Can the tile's 16-byte buffer loads be used? Needs 16-byte aligned A and B, row
-// strides and the K and N extents in whole 8-element chunks, and every in-tile
-// offset below the buffer range limit.
-bool vector_ok(int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, int bm, int bn, int bk) {
+// strides and the contiguous extent of each stored operand (K, or M / N for the
+// M/N-contiguous layouts) in whole 8-element chunks, and every in-tile offset below
+// the buffer range limit. ta / tb: A / B supplied transposed.
+bool vector_ok(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, int bm, int bn,
+               int bk, bool ta, bool tb) {
   if (((uintptr_t)A & 15) || ((uintptr_t)B & 15)) return false;
-  if ((lda & 7) || (ldb & 7) || (K & 7) || (N & 7)) return false;
-  if (((int64_t)(bm - 1) * lda + bk) * 2 >= kMaxRecords) return false;
-  if (((int64_t)(bk - 1) * ldb + bn) * 2 >= kMaxRecords) return false;
+  if ((lda & 7) || (ldb & 7)) return false;
+  if (((ta ? M : K) & 7) || ((tb ? K : N) & 7)) return false;
+  // largest in-tile byte offset: (tile rows - 1) * ld + row length of the stored tile
+  const int64_t a_rows = ta ? bk : bm, a_len = ta ? bm : bk;
+  const int64_t b_rows = tb ? bn : bk, b_len = tb ? bk : bn;
+  if (((a_rows - 1) * lda + a_len) * 2 >= kMaxRecords) return false;
+  if (((b_rows - 1) * ldb + b_len) * 2 >= kMaxRecords) return false;
   return true;
 }
 
@@ -77,9 +83,11 @@ int auto_macro(int64_t M, int64_t N) {
   return 3;
 }
 
-gemm_status_t plan_impl(const tgemm_handle* h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                        const void* B, int64_t ldb, const void* C, int64_t ldc, int dtype, gemm_plan_t* out) {
-  gemm_status_t st = gemm_check_args(M, N, K, A, lda, B, ldb, C, ldc, (gemm_dtype_t)dtype);
+gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, int64_t N, int64_t K, const void* A,
+                        int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc, int dtype,
+                        gemm_plan_t* out) {
+  gemm_status_t st = gemm_check_args_op((gemm_op_t)op_a, (gemm_op_t)op_b, M, N, K, A, lda, B, ldb, C, ldc,
+                                        (gemm_dtype_t)dtype);
   if (st != GEMM_OK) return st;
   gemm_plan_t p;
   std::memset(&p, 0, sizeof(p));
@@ -122,7 +130,8 @@ gemm_status_t plan_impl(const tgemm_handle* h, int64_t M, int64_t N, int64_t K, 
       p.lds_bytes = s.lds;
       p.kernel = 4;
     }
-    p.vector_loads = vector_ok(N, K, A, lda, B, ldb, p.tile_m, p.tile_n, p.tile_k) ? 1 : 0;
+    p.vector_loads =
+        vector_ok(M, N, K, A, lda, B, ldb, p.tile_m, p.tile_n, p.tile_k, op_a == GEMM_OP_T, op_b == GEMM_OP_T) ? 1 : 0;
   }
   p.split_k = 1;
   if (M == 0 || N == 0) {
@@ -170,24 +179,34 @@ const char* gemm_status_string(gemm_status_t s) {
     case GEMM_ERR_NO_DEVICE: return "GEMM_ERR_NO_DEVICE: no HIP device";
     case GEMM_ERR_ARCH: return "GEMM_ERR_ARCH: device is not gfx950";
     case GEMM_ERR_HIP: return "GEMM_ERR_HIP: HIP runtime or launch failure";
-    case GEMM_ERR_OUT_OF_MEMORY: return "GEMM_ERR_OUT_OF_MEMORY: host allocation failed";
+    case GEMM_ERR_OUT_OF_MEMORY: return "GEMM_ERR_OUT_OF_MEMORY: allocation of the handle or workspace failed";
     case GEMM_ERR_UNSUPPORTED_TILE: return "GEMM_ERR_UNSUPPORTED_TILE: no kernel has this tile for this dtype";
   }
   return "unknown status";
 }
 
-gemm_status_t gemm_check_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-                              int64_t ldb, const void* C, int64_t ldc, gemm_dtype_t dtype) {
+gemm_status_t gemm_check_args_op(gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K, const void* A,
+                                 int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc,
+                                 gemm_dtype_t dtype) {
   const int d = (int)dtype;
   if (d < GEMM_I32_I32 || d > GEMM_F16_F16) return GEMM_ERR_UNSUPPORTED_DTYPE;
+  if ((op_a != GEMM_OP_N && op_a != GEMM_OP_T) || (op_b != GEMM_OP_N && op_b != GEMM_OP_T))
+    return GEMM_ERR_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
   if (M > kI32Max || N > kI32Max || K > kI32Max) return GEMM_ERR_INVALID_ARG;
-  if (lda < max1(K) || ldb < max1(N) || ldc < max1(N)) return GEMM_ERR_INVALID_ARG;
+  // row length of each stored matrix: A is M x K (K x M transposed), B is K x N (N x K transposed)
+  const int64_t a_len = op_a == GEMM_OP_N ? K : M, b_len = op_b == GEMM_OP_N ? N : K;
+  if (lda < max1(a_len) || ldb < max1(b_len) || ldc < max1(N)) return GEMM_ERR_INVALID_ARG;
   if (lda > (int64_t)1 << 40 || ldb > (int64_t)1 << 40 || ldc > (int64_t)1 << 40) return GEMM_ERR_INVALID_ARG;
   if (M * K > 0 && A == nullptr) return GEMM_ERR_INVALID_ARG;
   if (K * N > 0 && B == nullptr) return GEMM_ERR_INVALID_ARG;
   if (M * N > 0 && C == nullptr) return GEMM_ERR_INVALID_ARG;
   return GEMM_OK;
+}
+
+gemm_status_t gemm_check_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                              int64_t ldb, const void* C, int64_t ldc, gemm_dtype_t dtype) {
+  return gemm_check_args_op(GEMM_OP_N, GEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc, dtype);
 }
 
 gemm_status_t gemm_create(gemm_handle_t* out) {
@@ -247,25 +266,35 @@ gemm_status_t gemm_set_split_k(gemm_handle_t h, int32_t splits) {
   return GEMM_OK;
 }
 
+gemm_status_t gemm_plan_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                           const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc,
+                           gemm_dtype_t dtype, gemm_plan_t* out) {
+  if (out == nullptr) return GEMM_ERR_INVALID_ARG;
+  if (h != nullptr && !is_live(h)) return GEMM_ERR_INVALID_ARG;
+  return plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, out);
+}
+
 gemm_status_t gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                         const void* B, int64_t ldb, const void* C, int64_t ldc, gemm_dtype_t dtype,
                         gemm_plan_t* out) {
-  if (out == nullptr) return GEMM_ERR_INVALID_ARG;
-  if (h != nullptr && !is_live(h)) return GEMM_ERR_INVALID_ARG;
-  return plan_impl(h, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, out);
+  return gemm_plan_op(h, GEMM_OP_N, GEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc, dtype, out);
 }
 
-gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                       const void* B, int64_t ldb, void* C, int64_t ldc, gemm_dtype_t dtype, void* stream) {
+gemm_status_t gemm_run_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                          const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                          gemm_dtype_t dtype, void* stream) {
   if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
   gemm_plan_t p;
-  gemm_status_t st = plan_impl(h, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &p);
+  gemm_status_t st = plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &p);
   if (st != GEMM_OK) return st;
+  const bool ta = op_a == GEMM_OP_T, tb = op_b == GEMM_OP_T;
   static const bool log = std::getenv("TGEMM_LOG") != nullptr;
   if (log)
-    std::fprintf(stderr, "tgemm: M=%lld N=%lld K=%lld dtype=%d kernel=%d tile=%dx%dx%d threads=%d vec=%d grid=%lld\n",
-                 (long long)M, (long long)N, (long long)K, (int)dtype, p.kernel, p.tile_m, p.tile_n, p.tile_k,
-                 p.threads, p.vector_loads, (long long)p.grid);
+    std::fprintf(stderr,
+                 "tgemm: op=%c%c M=%lld N=%lld K=%lld dtype=%d kernel=%d tile=%dx%dx%d threads=%d vec=%d grid=%lld "
+                 "split_k=%d\n",
+                 ta ? 'T' : 'N', tb ? 'T' : 'N', (long long)M, (long long)N, (long long)K, (int)dtype, p.kernel,
+                 p.tile_m, p.tile_n, p.tile_k, p.threads, p.vector_loads, (long long)p.grid, p.split_k);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   switch (p.kernel) {
@@ -279,8 +308,10 @@ gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const v
       a.M = (int)M;
       a.N = (int)N;
       a.K = (int)K;
-      a.lda = lda;
-      a.ldb = ldb;
+      a.sa_m = ta ? 1 : lda;
+      a.sa_k = ta ? lda : 1;
+      a.sb_k = tb ? 1 : ldb;
+      a.sb_n = tb ? ldb : 1;
       a.ldc = ldc;
       a.tm = p.tile_m;
       a.tn = p.tile_n;
@@ -324,17 +355,17 @@ gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const v
       a.kt_per_split = (int)cdiv(nk, splits);
       a.split_stride = (int64_t)M * N;
       if (p.kernel == 3) {
-        e = tg::launch_small(a, in_kind(dtype), out_kind(dtype), p.vector_loads != 0, s, p.grid);
+        e = tg::launch_small(a, in_kind(dtype), out_kind(dtype), p.vector_loads != 0, s, p.grid, ta, tb);
       } else if (splits == 1) {
         e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k), a, in_kind(dtype), out_kind(dtype),
-                             p.vector_loads != 0, s, p.grid, 1);
+                             p.vector_loads != 0, s, p.grid, 1, ta, tb);
       } else {
         // partial tiles (fp32, dense, ldc = N) into the workspace, then the ordered reduction
         tg::MacroArgs w = a;
         w.C = h->ws;
         w.ldc = N;
         e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k), w, in_kind(dtype), 0, p.vector_loads != 0, s,
-                             p.grid, splits);
+                             p.grid, splits, ta, tb);
         if (e == hipSuccess)
           e = tg::launch_splitk_reduce((const float*)h->ws, splits, C, ldc, (int)M, (int)N, out_kind(dtype), s);
       }
@@ -342,6 +373,11 @@ gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const v
     }
   }
   return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                       const void* B, int64_t ldb, void* C, int64_t ldc, gemm_dtype_t dtype, void* stream) {
+  return gemm_run_op(h, GEMM_OP_N, GEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc, dtype, stream);
 }
 
 }  // extern "C"

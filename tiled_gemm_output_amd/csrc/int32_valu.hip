@@ -7,7 +7,8 @@
 // matrices, uniform barriers and a guarded store (Mojo GPU puzzles, "Tiled Matrix
 // Multiplication", sections 3-6). Each thread keeps its C element in a register
 // for the whole reduction. Products and sums are unsigned 32-bit, i.e. they wrap
-// modulo 2^32, so the result does not depend on the order of the sum.
+// modulo 2^32, so the result does not depend on the order of the sum. A and B are
+// addressed through element strides, which covers operands supplied transposed.
 #include "device_common.h"
 #include "launch.h"
 
@@ -29,11 +30,11 @@ __global__ __launch_bounds__(1024) void i32_tile_kernel(I32Args p) {
   for (int k0 = 0; k0 < p.K; k0 += tk) {
     for (int q = t; q < tm * tk; q += nthreads) {
       const int r = q / tk, c = q % tk;
-      as[q] = (row0 + r < p.M && k0 + c < p.K) ? A[(int64_t)(row0 + r) * p.lda + k0 + c] : 0u;
+      as[q] = (row0 + r < p.M && k0 + c < p.K) ? A[(int64_t)(row0 + r) * p.sa_m + (int64_t)(k0 + c) * p.sa_k] : 0u;
     }
     for (int q = t; q < tk * tn; q += nthreads) {
       const int r = q / tn, c = q % tn;
-      bs[q] = (k0 + r < p.K && col0 + c < p.N) ? B[(int64_t)(k0 + r) * p.ldb + col0 + c] : 0u;
+      bs[q] = (k0 + r < p.K && col0 + c < p.N) ? B[(int64_t)(k0 + r) * p.sb_k + (int64_t)(col0 + c) * p.sb_n] : 0u;
     }
     __syncthreads();
     const int kmax = (p.K - k0) < tk ? (p.K - k0) : tk;

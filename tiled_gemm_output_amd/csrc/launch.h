@@ -27,20 +27,32 @@ struct MacroShape {
 constexpr int kNumMacroShapes = 5;
 extern const MacroShape kMacroShapes[kNumMacroShapes];
 
-// in: 0 = f16, 1 = bf16. out: 0 = f32, 1 = bf16, 2 = f16.
+// in: 0 = f16, 1 = bf16. out: 0 = f32, 1 = bf16, 2 = f16. ta: A is stored transposed
+// (K x M, row stride lda); tb: B is stored transposed (N x K, row stride ldb).
 hipError_t launch_macro(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
-                        int splits);
+                        int splits, bool ta, bool tb);
+// one operand layout each (nn: neither operand transposed, nt: B, tn: A, tt: both)
+hipError_t launch_macro_nn(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
+                           int splits);
+hipError_t launch_macro_nt(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
+                           int splits);
+hipError_t launch_macro_tn(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
+                           int splits);
+hipError_t launch_macro_tt(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
+                           int splits);
 // C[0:M, 0:N] = sum over s < splits of ws[s][M][N] (dense fp32 partials, summed in slice order),
 // rounded to the output format (out: 0 = f32, 1 = bf16, 2 = f16).
 hipError_t launch_splitk_reduce(const float* ws, int splits, void* C, int64_t ldc, int M, int N, int out, hipStream_t s);
-hipError_t launch_small(const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid);
+hipError_t launch_small(const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid, bool ta, bool tb);
 
 struct I32Args {
   const int32_t* A;
   const int32_t* B;
   int32_t* C;
   int M, N, K;
-  int64_t lda, ldb, ldc;
+  int64_t sa_m, sa_k;  // element (m, k) of op(A) is A[m * sa_m + k * sa_k]
+  int64_t sb_k, sb_n;  // element (k, n) of op(B) is B[k * sb_k + n * sb_n]
+  int64_t ldc;
   int tm, tn, tk, tiles_n;
 };
 hipError_t launch_i32(const I32Args& a, hipStream_t s, int64_t grid, int threads, int lds_bytes);

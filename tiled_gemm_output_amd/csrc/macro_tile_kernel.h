@@ -1,0 +1,485 @@
+// macro_tile_kernel.h -- the output-stationary macro-tile GEMM on gfx950 MFMA.
+//
+// One workgroup owns one BM x BN tile of C ("Reading a matrix multiply through its
+// tiles", section "Keep one output tile resident"): its fp32 accumulator lives in
+// the waves' registers for the whole reduction, the A (BM x BK) and B (BK x BN)
+// K-tiles of each step are staged through LDS, and the tile is written to C once.
+// Partial edge tiles use their actual ranges ("Edge tiles still matter"): loads
+// outside A or B read zeros, stores outside C are dropped, and every thread reaches
+// every barrier (the Mojo puzzle's manual kernel, sections 3-6, guards loads,
+// compute and store but never the barriers).
+//
+// Operand layouts. Each operand is either K-contiguous in memory (A as given, or
+// B supplied transposed, N x K) or M/N-contiguous (B as given, or A supplied
+// transposed, K x M); the Mojo puzzle page's section on transposed loading
+// describes reading a transposed operand through the shared tile. The two layouts
+// are staged differently (see Opnd) and deliver identical MFMA fragments.
+//
+// gfx950 design (differs from the pages' one-thread-per-element kernels):
+//  * waves of 64 lanes, each owning a (BM/WM) x (BN/WN) sub-tile computed with
+//    v_mfma_f32_32x32x16_{bf16,f16};
+//  * two LDS stages (double buffering: the loads of step k+1 are in flight while
+//    step k is multiplied), one barrier per step;
+//  * vector path: 16-byte buffer loads straight from global memory into LDS
+//    (buffer_load_dwordx4 ... lds), no register staging; out-of-range lanes use an
+//    offset beyond the buffer and receive zeros;
+//  * element path (unaligned pointers/leading dimensions, contiguous extents not a
+//    multiple of 8): guarded 16-bit loads into registers, then 16-byte LDS writes;
+//  * LDS layouts XOR-swizzled per 16-byte chunk so that the fragment reads
+//    (ds_read_b128 for K-contiguous tiles; ds_read_b64_tr_b16, which also performs
+//    the transpose MFMA needs, for M/N-contiguous tiles) hit distinct banks;
+//  * XCD-aware, grouped workgroup -> tile order (schedule_tile).
+#pragma once
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace tg {
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct MacroCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kWTM = BM / WM, kWTN = BN / WN;  // wave sub-tile
+  static constexpr int kFM = kWTM / 32, kFN = kWTN / 32;  // 32x32 MFMA blocks per wave
+  static constexpr int kABytes = BM * BK * 2, kBBytes = BK * BN * 2;
+  static constexpr int kSubsteps = BK / 16;
+  static constexpr int kLds = 2 * (kABytes + kBBytes);
+  static_assert(BK == 64, "four 16-deep substeps per K-step");
+  static_assert(kFM >= 1 && kFN >= 1 && kWTM % 32 == 0 && kWTN % 32 == 0, "wave tile must be a multiple of 32x32");
+  static_assert(kLds <= 160 * 1024, "LDS budget");
+};
+
+using Cfg256x256w8 = MacroCfg<256, 256, 64, 2, 4>;  // 8 waves, 128 x 64 per wave
+using Cfg256x256w4 = MacroCfg<256, 256, 64, 2, 2>;  // 4 waves, 128 x 128 per wave
+using Cfg256x128 = MacroCfg<256, 128, 64, 4, 2>;
+using Cfg128x128 = MacroCfg<128, 128, 64, 2, 2>;
+using Cfg64x64 = MacroCfg<64, 64, 64, 2, 2>;
+
+// Physical 16-byte chunk of logical chunk c in a K-contiguous row r (8 chunks per
+// row): c ^ swz_a(r). For any 16 consecutive rows starting at a multiple of 16 and
+// a fixed c, the 8-row halves see 8 distinct chunks, and rows of equal parity see
+// 8 distinct chunks.
+__device__ __forceinline__ int swz_a(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Physical chunk XOR for an M/N-contiguous row k (CH chunks per row). A transpose
+// read touches 4 consecutive rows x 2 (or 4) consecutive chunks; these masks keep
+// them on distinct banks.
+template <int CH>
+__device__ __forceinline__ int swz_b(int k) {
+  const int m = k & 3;
+  const int h = m == 0 ? 0 : (m == 1 ? 6 : (m == 2 ? 10 : 12));
+  return h & (CH - 1);
+}
+
+// One operand's K-tile in LDS and the lanes that move it. X is the operand's
+// extent along M (A) or N (B). KMAJ: K-contiguous in memory; the tile is stored
+// as X rows of BK values (128 bytes) and a fragment is one ds_read_b128 per lane.
+// Otherwise M/N-contiguous: BK rows of X values, and a fragment is two
+// ds_read_b64_tr_b16 per lane. Either way lane l of fragment f, substep s holds
+// position 32f + l%32 along X and reduction indices 16s + 8(l/32) .. +7, the
+// operand layout of v_mfma_f32_32x32x16.
+//
+// "Stored" rows and columns below are those of the matrix as it lies in memory:
+// for KMAJ a stored row is an X index and a stored column a K index, otherwise
+// the reverse.
+template <int X, int BK, bool KMAJ, int WAVES>
+struct Opnd {
+  static constexpr int kBytes = X * BK * 2;
+  static constexpr int kRow = KMAJ ? BK * 2 : X * 2;  // LDS row pitch in bytes
+  static constexpr int kChunks = kRow / 16;           // 16-byte chunks per row
+  static constexpr int kRowsPerBlock = 1024 / kRow;   // rows per 1 KiB DMA block
+  static constexpr int kPer = kBytes / 1024 / WAVES;  // DMA blocks per wave and stage
+  static constexpr int kReads = KMAJ ? 1 : 2;         // LDS reads per fragment
+  static_assert(!KMAJ || kChunks == 8, "K-contiguous swizzle assumes 8 chunks per row");
+  static_assert(KMAJ || (kRow <= 1024 && kChunks >= 8), "M/N-contiguous rows must tile 1 KiB, >= 8 chunks");
+  static_assert(kPer >= 1 && (kBytes / 1024) % WAVES == 0, "DMA blocks must divide among waves");
+
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (KMAJ)
+      return swz_a(r);
+    else
+      return swz_b<kChunks>(r);
+  }
+  // Tile row filled by lane l of DMA block t of wave w, and the logical chunk it
+  // carries (its 16 bytes land at physical chunk l % kChunks of that row).
+  __device__ static __forceinline__ int row(int w, int t, int l) { return (w * kPer + t) * kRowsPerBlock + l / kChunks; }
+  __device__ static __forceinline__ int chunk(int r, int l) { return (l % kChunks) ^ swz(r); }
+  // Reduction offset inside the K-tile of the data lane l of block t moves.
+  __device__ static __forceinline__ int kpos(int w, int t, int l) {
+    const int r = row(w, t, l);
+    return KMAJ ? 8 * chunk(r, l) : r;
+  }
+
+  // Byte offset of a fragment's first read for lane l (xoff: the wave's offset
+  // along X). For KMAJ, substep s is an XOR of s << 5 (the chunk pair 2s, 2s+1);
+  // otherwise rows 16s (+4) are added.
+  __device__ static __forceinline__ uint32_t frag(int xoff, int f, int l) {
+    if constexpr (KMAJ) {
+      const int r = xoff + 32 * f + (l & 31);
+      return (uint32_t)(r * kRow + (((l >> 5) ^ swz(r)) << 4));
+    } else {
+      const int g = l >> 4, jj = l & 15;
+      const int k = 8 * (g >> 1) + (jj >> 2);
+      const int n = xoff + 32 * f + 16 * (g & 1) + 4 * (jj & 3);
+      return (uint32_t)(k * kRow + (((n >> 3) ^ swz(k)) << 4) + (n & 7) * 2);
+    }
+  }
+  __device__ static __forceinline__ i32x4 read(TG_LDS char* base, uint32_t off, int s) {
+    if constexpr (KMAJ) {
+      asm volatile("" : "+v"(off));  // keep the XOR in the loop (hoisting it costs registers)
+      return *(TG_LDS i32x4*)(base + (off ^ (uint32_t)(s << 5)));
+    } else {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS s16x4*)(base + off + (16 * s) * kRow));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS s16x4*)(base + off + (16 * s + 4) * kRow));
+      const int2 l2 = __builtin_bit_cast(int2, lo), h2 = __builtin_bit_cast(int2, hi);
+      return i32x4{l2.x, l2.y, h2.x, h2.y};
+    }
+  }
+};
+
+// Loads: kLoadElem = guarded element loads staged in registers; kLoadVec = 16-byte
+// direct loads, the last K-tile may be partial; kLoadVecFull = 16-byte direct loads,
+// K is a multiple of BK.
+enum { kLoadElem = 0, kLoadVec = 1, kLoadVecFull = 2 };
+
+template <int N>
+struct IC {
+  static constexpr int value = N;
+};
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IC<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Workgroup barrier without a memory fence. The waits the pipeline needs are
+// explicit s_waitcnt instructions placed before it (a fenced barrier would also
+// wait for every load in flight); the empty asm statements keep the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Instruction order inside one scheduling region: each MFMA is followed by the
+// next share of the region's LDS reads and global loads, so that reads for the
+// next substep and refill loads are issued early and spread over the MFMAs.
+template <int NM, int NR, int NV>
+__device__ __forceinline__ void interleave() {
+  constexpr int rper = NM > 0 ? (NR + NM - 1) / NM : 0;
+  constexpr int vper = NM > 0 ? (NV + NM - 1) / NM : 0;
+  static_for<0, NM>([&](auto q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    constexpr int r = NR - q.value * rper;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r < rper ? r : rper, 0);  // DS read
+    constexpr int v = NV - q.value * vper;
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v < vper ? v : vper, 0);  // VMEM read
+  });
+}
+
+// TA: A is supplied transposed (stored K x M, lda >= M); TB: B is supplied
+// transposed (stored N x K, ldb >= K). C is always M x N row-major.
+template <class Cfg, int IN, int OUT, int LOAD, bool TA, bool TB>
+__global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs p) {
+  constexpr bool VEC = LOAD != kLoadElem;
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+  constexpr int FM = Cfg::kFM, FN = Cfg::kFN;
+  using OA = Opnd<BM, BK, !TA, Cfg::kWaves>;
+  using OB = Opnd<BN, BK, TB, Cfg::kWaves>;
+  constexpr int kAPer = OA::kPer, kBPer = OB::kPer;
+  constexpr int NR = FM * OA::kReads + FN * OB::kReads;  // LDS reads per substep
+  constexpr int NM = FM * FN;                            // MFMAs per substep
+  __shared__ __attribute__((aligned(1024))) char sA0[Cfg::kABytes];
+  __shared__ __attribute__((aligned(1024))) char sA1[Cfg::kABytes];
+  __shared__ __attribute__((aligned(1024))) char sB0[Cfg::kBBytes];
+  __shared__ __attribute__((aligned(1024))) char sB1[Cfg::kBBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+
+  int tile_m, tile_n;
+  schedule_tile(blockIdx.x, gridDim.x, p.tiles_m, p.group_m, tile_m, tile_n);
+  const int row0 = tile_m * BM, col0 = tile_n * BN;
+  const int M = p.M, N = p.N, K = p.K;
+  const int64_t lda = p.lda, ldb = p.ldb;
+  // K-tiles of this workgroup: [kt_base, kt_base + nk) (all of them without split-K)
+  const int kt_base = blockIdx.y * p.kt_per_split;
+  const int nk_all = (K + BK - 1) / BK;
+  const int nk = (nk_all - kt_base) < p.kt_per_split ? (nk_all - kt_base) : p.kt_per_split;
+
+  // ---------------- loader geometry ----------------
+  // Lane l of DMA block t fills tile row OX::row(wave, t, l) at physical chunk
+  // l % kChunks; the direct loads write lane l's 16 bytes to block base + 16*l
+  // and the element path writes the same slot. Per-lane byte offsets from the
+  // K-tile's origin; the bound that does not depend on the K-tile (the M or N
+  // extent) is folded in here as an out-of-range offset.
+  uint32_t a_off[kAPer], b_off[kBPer];
+  if constexpr (VEC) {
+#pragma unroll
+    for (int t = 0; t < kAPer; ++t) {
+      const int r = OA::row(wave, t, lane), c = OA::chunk(r, lane);
+      const bool in = TA ? (row0 + 8 * c < M) : (row0 + r < M);
+      a_off[t] = in ? (uint32_t)(((int64_t)r * lda + 8 * c) * 2) : kOutOfRange;
+    }
+#pragma unroll
+    for (int t = 0; t < kBPer; ++t) {
+      const int r = OB::row(wave, t, lane), c = OB::chunk(r, lane);
+      const bool in = TB ? (col0 + r < N) : (col0 + 8 * c < N);
+      b_off[t] = in ? (uint32_t)(((int64_t)r * ldb + 8 * c) * 2) : kOutOfRange;
+    }
+  }
+  // Origin of K-tile k0 (element offset) in each stored matrix, and the extent of
+  // the stored matrix from there on (bytes), for the buffer descriptors.
+  auto a_origin = [&](int k0) { return TA ? (int64_t)k0 * lda + row0 : (int64_t)row0 * lda + k0; };
+  auto b_origin = [&](int k0) { return TB ? (int64_t)col0 * ldb + k0 : (int64_t)k0 * ldb + col0; };
+  auto a_extent = [&](int k0) {
+    return (TA ? (int64_t)(K - 1 - k0) * lda + (M - row0) : (int64_t)(M - 1 - row0) * lda + (K - k0)) * 2;
+  };
+  auto b_extent = [&](int k0) {
+    return (TB ? (int64_t)(N - 1 - col0) * ldb + (K - k0) : (int64_t)(K - 1 - k0) * ldb + (N - col0)) * 2;
+  };
+
+  // Vector path: issue the direct loads of K-tile kt into a stage. Branch-free: a
+  // K-tile outside [0, nk) gets a zero-length buffer, so every lane reads zeros and
+  // no memory is touched (this keeps the compiler's tracking of which stage each
+  // load writes exact, so it adds no waits before reads of the other stage).
+  auto issue_loads = [&](TG_LDS char* sa, TG_LDS char* sb, int kt) {
+    const bool ok = (unsigned)kt < (unsigned)nk;
+    const int k0 = ok ? (kt_base + kt) * BK : 0;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_origin(k0), ok ? a_extent(k0) : 0);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + b_origin(k0), ok ? b_extent(k0) : 0);
+#pragma unroll
+    for (int t = 0; t < kAPer; ++t) {
+      uint32_t off = a_off[t];
+      if constexpr (LOAD == kLoadVec) off = (k0 + OA::kpos(wave, t, lane) < K) ? off : kOutOfRange;
+      load_lds_x4(ra, sa + (wave * kAPer + t) * 1024, off);
+    }
+#pragma unroll
+    for (int t = 0; t < kBPer; ++t) {
+      uint32_t off = b_off[t];
+      if constexpr (LOAD == kLoadVec) off = (k0 + OB::kpos(wave, t, lane) < K) ? off : kOutOfRange;
+      load_lds_x4(rb, sb + (wave * kBPer + t) * 1024, off);
+    }
+  };
+
+  // Element path: guarded 16-bit loads of K-tile kt into registers (zeros outside
+  // the matrices and for kt outside [0, nk)), and their 16-byte LDS writes. Lane l
+  // of block t reads 8 consecutive elements of one stored row.
+  i32x4 a_reg[kAPer], b_reg[kBPer];
+  auto fetch8 = [](const uint16_t* src, bool row_ok, int col, int cols) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = (row_ok && col + 2 * e < cols) ? src[2 * e] : 0u;
+      const uint32_t hi = (row_ok && col + 2 * e + 1 < cols) ? src[2 * e + 1] : 0u;
+      w[e] = lo | (hi << 16);
+    }
+    return i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+  };
+  auto fetch_regs = [&](int kt) {
+    const bool ok = (unsigned)kt < (unsigned)nk;
+    const int k0 = (kt_base + kt) * BK;
+#pragma unroll
+    for (int t = 0; t < kAPer; ++t) {
+      const int r = OA::row(wave, t, lane), c = OA::chunk(r, lane);
+      // stored row / column of A: (m, k) as given, (k, m) transposed
+      const int sr = TA ? k0 + r : row0 + r, sc = TA ? row0 + 8 * c : k0 + 8 * c;
+      const int rows = TA ? K : M, cols = TA ? M : K;
+      a_reg[t] = fetch8(p.A + (int64_t)sr * lda + sc, ok && sr < rows, sc, cols);
+    }
+#pragma unroll
+    for (int t = 0; t < kBPer; ++t) {
+      const int r = OB::row(wave, t, lane), c = OB::chunk(r, lane);
+      // stored row / column of B: (k, n) as given, (n, k) transposed
+      const int sr = TB ? col0 + r : k0 + r, sc = TB ? k0 + 8 * c : col0 + 8 * c;
+      const int rows = TB ? N : K, cols = TB ? K : N;
+      b_reg[t] = fetch8(p.B + (int64_t)sr * ldb + sc, ok && sr < rows, sc, cols);
+    }
+  };
+  auto store_regs = [&](TG_LDS char* sa, TG_LDS char* sb) {
+#pragma unroll
+    for (int t = 0; t < kAPer; ++t) *(TG_LDS i32x4*)(sa + (wave * kAPer + t) * 1024 + lane * 16) = a_reg[t];
+#pragma unroll
+    for (int t = 0; t < kBPer; ++t) *(TG_LDS i32x4*)(sb + (wave * kBPer + t) * 1024 + lane * 16) = b_reg[t];
+  };
+
+  // ---------------- fragment addressing ----------------
+  uint32_t a_frag[FM], b_frag[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) a_frag[i] = OA::frag(wm * Cfg::kWTM, i, lane);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) b_frag[j] = OB::frag(wn * Cfg::kWTN, j, lane);
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+  // Fragments of substep s (16 reduction indices), read in the order the MFMAs
+  // (row-major over the i x j blocks) consume them: a[0], every b[j], a[1..].
+  auto read_frags = [&](TG_LDS char* sa, TG_LDS char* sb, int s, i32x4(&a)[FM], i32x4(&b)[FN]) {
+    a[0] = OA::read(sa, a_frag[0], s);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b[j] = OB::read(sb, b_frag[j], s);
+#pragma unroll
+    for (int i = 1; i < FM; ++i) a[i] = OA::read(sa, a_frag[i], s);
+  };
+  // MFMAs of one substep; half 0 = block rows [0, FM/2), half 1 = the rest.
+  auto mfma_rows = [&](const i32x4(&a)[FM], const i32x4(&b)[FN], int i0, int i1) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      if (i >= i0 && i < i1)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<IN>(a[i], b[j], acc[i][j]);
+  };
+
+  TG_LDS char* pA0 = (TG_LDS char*)sA0;
+  TG_LDS char* pA1 = (TG_LDS char*)sA1;
+  TG_LDS char* pB0 = (TG_LDS char*)sB0;
+  TG_LDS char* pB1 = (TG_LDS char*)sB1;
+
+  // ---------------- main loop ----------------
+  // Two stages; K-tile kt0 + st lives in stage st % 2. Each step multiplies its
+  // stage in four substeps; the reads of substep s+1 are issued among the MFMAs
+  // of substep s. The barrier that ends the step sits after the first half of the
+  // last substep's MFMAs: once every wave is past it, the stage just consumed is
+  // refilled with K-tile st + 2 and the next stage's first fragments are read,
+  // both covered by the second half of those MFMAs. When the number of K-tiles is
+  // odd, a zero K-tile (index -1) is prepended so that every step is unconditional.
+  const int kt0 = (nk & 1) ? -1 : 0;
+  const int nsteps = nk - kt0;  // even, >= 2
+  i32x4 fa[FM], fb[FN], ga[FM], gb[FN];
+  if constexpr (VEC) {
+    issue_loads(pA0, pB0, kt0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  } else {
+    fetch_regs(kt0);
+    store_regs(pA0, pB0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  }
+  barrier_nofence();
+  if constexpr (VEC)
+    issue_loads(pA1, pB1, kt0 + 1);
+  else
+    fetch_regs(kt0 + 1);
+  read_frags(pA0, pB0, 0, fa, fb);
+
+  auto step = [&](TG_LDS char* sa, TG_LDS char* sb, TG_LDS char* na, TG_LDS char* nb, int st) {
+    read_frags(sa, sb, 1, ga, gb);
+    mfma_rows(fa, fb, 0, FM);
+    interleave<NM, NR, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(sa, sb, 2, fa, fb);
+    mfma_rows(ga, gb, 0, FM);
+    interleave<NM, NR, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(sa, sb, 3, ga, gb);
+    mfma_rows(fa, fb, 0, FM);
+    interleave<NM, NR, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_rows(ga, gb, 0, FM / 2);
+    __builtin_amdgcn_sched_barrier(0);
+    // the next stage must be complete in every wave before anyone reads it
+    if constexpr (VEC) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of K-tile st + 1 landed
+    } else {
+      store_regs(na, nb);                  // K-tile st + 1, fetched one step ago
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    }
+    barrier_nofence();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (VEC)
+      issue_loads(sa, sb, kt0 + st + 2);  // out of range on the last two steps: zero-length, no traffic
+    else
+      fetch_regs(kt0 + st + 2);
+    read_frags(na, nb, 0, fa, fb);
+    mfma_rows(ga, gb, FM / 2, FM);
+    interleave<(FM - FM / 2) * FN, NR, VEC ? kAPer + kBPer : 0>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int st = 0; st < nsteps; st += 2) {
+    step(pA0, pB0, pA1, pB1, st);
+    step(pA1, pB1, pA0, pB0, st + 1);
+  }
+  if constexpr (VEC) __builtin_amdgcn_s_waitcnt(0x0F70);  // trailing loads land before LDS is released
+
+  // ---------------- epilogue: write the C tile once ----------------
+  // acc[i][j][v] holds row 32i + 8*(v/4) + 4*(lane/32) + v%4, column 32j + lane%32
+  // of the wave tile. Interior tiles store without bounds checks; edge tiles drop
+  // the elements outside C. With split-K, slice y writes its partial tile at
+  // C + y * split_stride.
+  const int64_t ldc = p.ldc;
+  char* const Cout = (char*)p.C + (int64_t)blockIdx.y * p.split_stride * (OUT == OUT_F32 ? 4 : 2);
+  const bool interior = row0 + BM <= M && col0 + BN <= N;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int rb = row0 + wm * Cfg::kWTM + 32 * i + 4 * (lane >> 5);
+      const int col = col0 + wn * Cfg::kWTN + 32 * j + (lane & 31);
+      const int64_t base = (int64_t)rb * ldc + col;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int dr = 8 * (v >> 2) + (v & 3);
+        if (interior || (rb + dr < M && col < N)) {
+          const int64_t off = base + (int64_t)dr * ldc;
+          const float x = acc[i][j][v];
+          if constexpr (OUT == OUT_F32)
+            ((float*)Cout)[off] = x;
+          else if constexpr (OUT == OUT_BF16)
+            ((uint16_t*)Cout)[off] = f32_to_bf16_rne(x);
+          else
+            ((uint16_t*)Cout)[off] = f32_to_f16_rne(x);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host-side instantiation and launch of one operand layout
+
+template <class Cfg, int IN, int OUT, bool TA, bool TB>
+static hipError_t launch_cfg(const MacroArgs& a, bool vec, hipStream_t stream, int64_t grid, int splits) {
+  const dim3 g((unsigned)grid, (unsigned)splits), b(Cfg::kThreads);
+  if (!vec)
+    hipLaunchKernelGGL((macro_tile_kernel<Cfg, IN, OUT, kLoadElem, TA, TB>), g, b, 0, stream, a);
+  else if (a.K % Cfg::BK == 0)
+    hipLaunchKernelGGL((macro_tile_kernel<Cfg, IN, OUT, kLoadVecFull, TA, TB>), g, b, 0, stream, a);
+  else
+    hipLaunchKernelGGL((macro_tile_kernel<Cfg, IN, OUT, kLoadVec, TA, TB>), g, b, 0, stream, a);
+  return hipGetLastError();
+}
+
+template <class Cfg, bool TA, bool TB>
+static hipError_t launch_dtype(const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
+                               int splits) {
+  if (in == IN_BF16 && out == OUT_F32) return launch_cfg<Cfg, IN_BF16, OUT_F32, TA, TB>(a, vec, s, grid, splits);
+  if (in == IN_BF16 && out == OUT_BF16) return launch_cfg<Cfg, IN_BF16, OUT_BF16, TA, TB>(a, vec, s, grid, splits);
+  if (in == IN_F16 && out == OUT_F32) return launch_cfg<Cfg, IN_F16, OUT_F32, TA, TB>(a, vec, s, grid, splits);
+  if (in == IN_F16 && out == OUT_F16) return launch_cfg<Cfg, IN_F16, OUT_F16, TA, TB>(a, vec, s, grid, splits);
+  return hipErrorInvalidValue;
+}
+
+template <bool TA, bool TB>
+static hipError_t launch_layout(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
+                                int splits) {
+  switch (shape) {
+    case 0: return launch_dtype<Cfg256x256w8, TA, TB>(a, in, out, vec, s, grid, splits);
+    case 1: return launch_dtype<Cfg256x128, TA, TB>(a, in, out, vec, s, grid, splits);
+    case 2: return launch_dtype<Cfg128x128, TA, TB>(a, in, out, vec, s, grid, splits);
+    case 3: return launch_dtype<Cfg64x64, TA, TB>(a, in, out, vec, s, grid, splits);
+    case 4: return launch_dtype<Cfg256x256w4, TA, TB>(a, in, out, vec, s, grid, splits);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tg

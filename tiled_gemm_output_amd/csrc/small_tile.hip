@@ -8,15 +8,52 @@
 //
 // The step structure is the macro-tile kernel's, scaled down: two LDS stages, a
 // direct global->LDS load of each 1 KiB tile (one 16-byte buffer load per lane) or
-// an element-wise guarded load when 16-byte loads are not possible, an A fragment
-// read with ds_read_b128 and a B fragment read with two ds_read_b64_tr_b16.
+// an element-wise guarded load when 16-byte loads are not possible, and fragment
+// reads with ds_read_b128 (K-contiguous operands) or two ds_read_b64_tr_b16
+// (M/N-contiguous operands: B as given, A supplied transposed).
 #include "device_common.h"
 #include "launch.h"
 
 namespace tg {
 
-template <int IN, int OUT, bool VEC>
+// One 1 KiB operand K-tile: 16 positions along M (A) or N (B) by 32 along K.
+// KMAJ (stored K-contiguous: A as given, B transposed): 16 LDS rows of 32 values
+// (64 bytes), lane l moves row l/4, chunk l%4, and a fragment is one ds_read_b128.
+// Otherwise (M/N-contiguous: B as given, A transposed): 32 rows of 16 values
+// (32 bytes), lane l moves row l/2, chunk l%2, and a fragment is two
+// ds_read_b64_tr_b16. Either way lane l ends up with position l%16 and reduction
+// indices 8*(l/16) .. +7, the operand layout of v_mfma_f32_16x16x32.
+template <bool KMAJ>
+struct SmallOpnd {
+  static constexpr int kRow = KMAJ ? 64 : 32;
+  static constexpr int kChunks = kRow / 16;
+  __device__ static __forceinline__ int row(int l) { return l / kChunks; }
+  __device__ static __forceinline__ int chunk(int l) { return l % kChunks; }
+  __device__ static __forceinline__ uint32_t frag(int l) {
+    if constexpr (KMAJ) {
+      return (uint32_t)((l & 15) * 64 + (l >> 4) * 16);
+    } else {
+      const int g = l >> 4, jj = l & 15;
+      return (uint32_t)((8 * g + (jj >> 2)) * 32 + 4 * (jj & 3) * 2);
+    }
+  }
+  __device__ static __forceinline__ i32x4 read(TG_LDS char* base, uint32_t off) {
+    if constexpr (KMAJ) {
+      return *(TG_LDS i32x4*)(base + off);
+    } else {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS s16x4*)(base + off));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS s16x4*)(base + off + 4 * 32));
+      const int2 l2 = __builtin_bit_cast(int2, lo), h2 = __builtin_bit_cast(int2, hi);
+      return i32x4{l2.x, l2.y, h2.x, h2.y};
+    }
+  }
+};
+
+// TA: A is supplied transposed (K x M); TB: B is supplied transposed (N x K).
+template <int IN, int OUT, bool VEC, bool TA, bool TB>
 __global__ __launch_bounds__(64) void small_tile_kernel(MacroArgs p) {
+  using OA = SmallOpnd<!TA>;
+  using OB = SmallOpnd<TB>;
   __shared__ __attribute__((aligned(1024))) char sA0[1024];
   __shared__ __attribute__((aligned(1024))) char sA1[1024];
   __shared__ __attribute__((aligned(1024))) char sB0[1024];
@@ -28,41 +65,42 @@ __global__ __launch_bounds__(64) void small_tile_kernel(MacroArgs p) {
   const int64_t lda = p.lda, ldb = p.ldb;
   const int nk = (K + 31) / 32;
 
-  // loader: lane l moves A row l/4, chunk l%4 (64-byte rows) and B row l/2, chunk l%2 (32-byte rows)
-  const int ar = lane >> 2, ac = lane & 3;
-  const int bk = lane >> 1, bc = lane & 1;
-  const uint32_t a_off = (row0 + ar < M) ? (uint32_t)(((int64_t)ar * lda + 8 * ac) * 2) : kOutOfRange;
-  const uint32_t b_off = (col0 + 8 * bc < N) ? (uint32_t)(((int64_t)bk * ldb + 8 * bc) * 2) : kOutOfRange;
+  // Lane l moves 8 consecutive elements of one stored row of each operand: tile
+  // row r, chunk c. Stored (row, column) of the K-tile's origin and the stored
+  // matrix's extents: A is (m, k) as given, (k, m) transposed; B is (k, n) as
+  // given, (n, k) transposed.
+  const int ar = OA::row(lane), ac = OA::chunk(lane);
+  const int br = OB::row(lane), bc = OB::chunk(lane);
+  const int a_rows = TA ? K : M, a_cols = TA ? M : K;
+  const int b_rows = TB ? N : K, b_cols = TB ? K : N;
   i32x4 a_reg, b_reg;
 
+  // 16 bytes of a stored row into one lane: direct to LDS (vector path; zeros
+  // outside the matrix via an out-of-range offset) or guarded element loads.
+  auto load8 = [&](const uint16_t* base, int64_t ld, int r0, int c0, int rows, int cols, int r, int c,
+                   TG_LDS char* dst, i32x4& reg) {
+    const int sr = r0 + r, sc = c0 + 8 * c;
+    if constexpr (VEC) {
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(base + (int64_t)r0 * ld + c0, ((int64_t)(rows - 1 - r0) * ld + (cols - c0)) * 2);
+      const uint32_t off = (sr < rows && sc < cols) ? (uint32_t)(((int64_t)r * ld + 8 * c) * 2) : kOutOfRange;
+      load_lds_x4(rs, dst, off);
+    } else {
+      const uint16_t* src = base + (int64_t)sr * ld + sc;
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = (sr < rows && sc + 2 * e < cols) ? src[2 * e] : 0u;
+        const uint32_t hi = (sr < rows && sc + 2 * e + 1 < cols) ? src[2 * e + 1] : 0u;
+        w[e] = lo | (hi << 16);
+      }
+      reg = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    }
+  };
   auto load_tile = [&](TG_LDS char* sa, TG_LDS char* sb, int kt) {
     const int k0 = kt * 32;
-    if constexpr (VEC) {
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + (int64_t)row0 * lda + k0, ((int64_t)(M - 1 - row0) * lda + (K - k0)) * 2);
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + (int64_t)k0 * ldb + col0, ((int64_t)(K - 1 - k0) * ldb + (N - col0)) * 2);
-      load_lds_x4(ra, sa, (k0 + 8 * ac < K) ? a_off : kOutOfRange);
-      load_lds_x4(rb, sb, (k0 + bk < K) ? b_off : kOutOfRange);
-    } else {
-      uint32_t w[4];
-      const int gr = row0 + ar, gk = k0 + 8 * ac;
-      const uint16_t* sa_src = p.A + (int64_t)gr * lda + gk;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (gr < M && gk + 2 * e < K) ? sa_src[2 * e] : 0u;
-        const uint32_t hi = (gr < M && gk + 2 * e + 1 < K) ? sa_src[2 * e + 1] : 0u;
-        w[e] = lo | (hi << 16);
-      }
-      a_reg = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-      const int gkb = k0 + bk, gc = col0 + 8 * bc;
-      const uint16_t* sb_src = p.B + (int64_t)gkb * ldb + gc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (gkb < K && gc + 2 * e < N) ? sb_src[2 * e] : 0u;
-        const uint32_t hi = (gkb < K && gc + 2 * e + 1 < N) ? sb_src[2 * e + 1] : 0u;
-        w[e] = lo | (hi << 16);
-      }
-      b_reg = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-    }
+    load8(p.A, lda, TA ? k0 : row0, TA ? row0 : k0, a_rows, a_cols, ar, ac, sa, a_reg);
+    load8(p.B, ldb, TB ? col0 : k0, TB ? k0 : col0, b_rows, b_cols, br, bc, sb, b_reg);
   };
   auto commit_tile = [&](TG_LDS char* sa, TG_LDS char* sb) {
     if constexpr (VEC) {
@@ -73,17 +111,10 @@ __global__ __launch_bounds__(64) void small_tile_kernel(MacroArgs p) {
     }
   };
 
-  // fragments: A row lane%16, chunk lane/16; B transpose read of rows 8g + jj/4 (+4), column 4*(jj%4)
-  const uint32_t a_frag = (uint32_t)((lane & 15) * 64 + (lane >> 4) * 16);
-  const int g = lane >> 4, jj = lane & 15;
-  const uint32_t b_frag = (uint32_t)((8 * g + (jj >> 2)) * 32 + 4 * (jj & 3) * 2);
+  const uint32_t a_frag = OA::frag(lane), b_frag = OB::frag(lane);
   f32x4 acc = f32x4{};
   auto compute_tile = [&](TG_LDS char* sa, TG_LDS char* sb) {
-    const i32x4 a = *(TG_LDS i32x4*)(sa + a_frag);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS s16x4*)(sb + b_frag));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TG_LDS s16x4*)(sb + b_frag + 4 * 32));
-    const int2 l2 = __builtin_bit_cast(int2, lo), h2 = __builtin_bit_cast(int2, hi);
-    acc = mfma16<IN>(a, i32x4{l2.x, l2.y, h2.x, h2.y}, acc);
+    acc = mfma16<IN>(OA::read(sa, a_frag), OB::read(sb, b_frag), acc);
   };
 
   TG_LDS char* pA0 = (TG_LDS char*)sA0;
@@ -123,21 +154,29 @@ __global__ __launch_bounds__(64) void small_tile_kernel(MacroArgs p) {
   }
 }
 
-template <int IN, int OUT>
+template <int IN, int OUT, bool TA, bool TB>
 static hipError_t launch_small_t(const MacroArgs& a, bool vec, hipStream_t s, int64_t grid) {
   if (vec)
-    hipLaunchKernelGGL((small_tile_kernel<IN, OUT, true>), dim3((unsigned)grid), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((small_tile_kernel<IN, OUT, true, TA, TB>), dim3((unsigned)grid), dim3(64), 0, s, a);
   else
-    hipLaunchKernelGGL((small_tile_kernel<IN, OUT, false>), dim3((unsigned)grid), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((small_tile_kernel<IN, OUT, false, TA, TB>), dim3((unsigned)grid), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_small(const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid) {
-  if (in == IN_BF16 && out == OUT_F32) return launch_small_t<IN_BF16, OUT_F32>(a, vec, s, grid);
-  if (in == IN_BF16 && out == OUT_BF16) return launch_small_t<IN_BF16, OUT_BF16>(a, vec, s, grid);
-  if (in == IN_F16 && out == OUT_F32) return launch_small_t<IN_F16, OUT_F32>(a, vec, s, grid);
-  if (in == IN_F16 && out == OUT_F16) return launch_small_t<IN_F16, OUT_F16>(a, vec, s, grid);
+template <bool TA, bool TB>
+static hipError_t launch_small_layout(const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid) {
+  if (in == IN_BF16 && out == OUT_F32) return launch_small_t<IN_BF16, OUT_F32, TA, TB>(a, vec, s, grid);
+  if (in == IN_BF16 && out == OUT_BF16) return launch_small_t<IN_BF16, OUT_BF16, TA, TB>(a, vec, s, grid);
+  if (in == IN_F16 && out == OUT_F32) return launch_small_t<IN_F16, OUT_F32, TA, TB>(a, vec, s, grid);
+  if (in == IN_F16 && out == OUT_F16) return launch_small_t<IN_F16, OUT_F16, TA, TB>(a, vec, s, grid);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_small(const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid, bool ta, bool tb) {
+  if (!ta && !tb) return launch_small_layout<false, false>(a, in, out, vec, s, grid);
+  if (!ta && tb) return launch_small_layout<false, true>(a, in, out, vec, s, grid);
+  if (ta && !tb) return launch_small_layout<true, false>(a, in, out, vec, s, grid);
+  return launch_small_layout<true, true>(a, in, out, vec, s, grid);
 }
 
 }  // namespace tg

@@ -19,6 +19,8 @@ LIBRARY = os.path.join(HERE, "libtgemm.so")
 
 # gemm_status_t
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED_DTYPE, ERR_NO_DEVICE, ERR_ARCH, ERR_HIP, ERR_OUT_OF_MEMORY, ERR_UNSUPPORTED_TILE = range(8)
+# gemm_op_t
+OP_N, OP_T = 0, 1
 # gemm_dtype_t
 I32_I32, F16_F32, BF16_F32, BF16_BF16, F16_F16 = range(5)
 DTYPES = {"i32": I32_I32, "f16_f32": F16_F32, "bf16_f32": BF16_F32, "bf16_bf16": BF16_BF16, "f16_f16": F16_F16}
@@ -26,8 +28,8 @@ IN_BYTES = {I32_I32: 4, F16_F32: 2, BF16_F32: 2, BF16_BF16: 2, F16_F16: 2}
 OUT_BYTES = {I32_I32: 4, F16_F32: 4, BF16_F32: 4, BF16_BF16: 2, F16_F16: 2}
 KERNEL_NAMES = {0: "none", 1: "zero_fill", 2: "int32_valu", 3: "mfma_16x16x32_one_wave", 4: "mfma_macro_tile"}
 
-EXPORTS = ["gemm_create", "gemm_run", "gemm_destroy", "gemm_set_tile", "gemm_set_split_k", "gemm_check_args",
-           "gemm_plan", "gemm_status_string"]
+EXPORTS = ["gemm_create", "gemm_run", "gemm_run_op", "gemm_destroy", "gemm_set_tile", "gemm_set_split_k",
+           "gemm_check_args", "gemm_check_args_op", "gemm_plan", "gemm_plan_op", "gemm_status_string"]
 
 
 class GemmPlan(ctypes.Structure):
@@ -63,6 +65,8 @@ def load(path: str = LIBRARY):
     lib.gemm_create.restype = i32
     lib.gemm_run.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, vp]
     lib.gemm_run.restype = i32
+    lib.gemm_run_op.argtypes = [vp, i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, vp]
+    lib.gemm_run_op.restype = i32
     lib.gemm_destroy.argtypes = [vp]
     lib.gemm_destroy.restype = i32
     lib.gemm_set_tile.argtypes = [vp, i32, i32, i32]
@@ -71,8 +75,12 @@ def load(path: str = LIBRARY):
     lib.gemm_set_split_k.restype = i32
     lib.gemm_check_args.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32]
     lib.gemm_check_args.restype = i32
+    lib.gemm_check_args_op.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32]
+    lib.gemm_check_args_op.restype = i32
     lib.gemm_plan.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, ctypes.POINTER(GemmPlan)]
     lib.gemm_plan.restype = i32
+    lib.gemm_plan_op.argtypes = [vp, i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, ctypes.POINTER(GemmPlan)]
+    lib.gemm_plan_op.restype = i32
     lib.gemm_status_string.argtypes = [i32]
     lib.gemm_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -111,13 +119,28 @@ def gemm_run(h, M, N, K, A, lda, B, ldb, C, ldc, dtype, stream=None) -> int:
     return load().gemm_run(h, M, N, K, A, lda, B, ldb, C, ldc, int(dtype), stream)
 
 
+def gemm_run_op(h, op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, dtype, stream=None) -> int:
+    return load().gemm_run_op(h, int(op_a), int(op_b), M, N, K, A, lda, B, ldb, C, ldc, int(dtype), stream)
+
+
 def gemm_check_args(M, N, K, A, lda, B, ldb, C, ldc, dtype) -> int:
     return load().gemm_check_args(M, N, K, A, lda, B, ldb, C, ldc, int(dtype))
+
+
+def gemm_check_args_op(op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, dtype) -> int:
+    return load().gemm_check_args_op(int(op_a), int(op_b), M, N, K, A, lda, B, ldb, C, ldc, int(dtype))
 
 
 def gemm_plan(h, M, N, K, A, lda, B, ldb, C, ldc, dtype) -> dict:
     p = GemmPlan()
     check(load().gemm_plan(h, M, N, K, A, lda, B, ldb, C, ldc, int(dtype), ctypes.byref(p)), "gemm_plan")
+    return p.as_dict()
+
+
+def gemm_plan_op(h, op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, dtype) -> dict:
+    p = GemmPlan()
+    check(load().gemm_plan_op(h, int(op_a), int(op_b), M, N, K, A, lda, B, ldb, C, ldc, int(dtype), ctypes.byref(p)),
+          "gemm_plan_op")
     return p.as_dict()
 
 
