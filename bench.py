@@ -232,6 +232,8 @@ def main() -> int:
                    "threads": plan["threads"],
                    "vector_loads": plan["vector_loads"], "kernel_source_sha": sha},
         "pct_of_mfma_peak": 100.0 * value / PEAK_MFMA_16BIT_TFLOPS,
+        "launch_us": {"mean": 1e3 * launch_ms, "median": 1e3 * float(np.median(per_launch_ms)),
+                      "min": 1e3 * float(np.min(per_launch_ms))},
         "roofline": roof,
         "cpu_baseline": None,
     }

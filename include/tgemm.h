@@ -88,6 +88,28 @@ typedef struct {
                                      slices whose fp32 partial tiles a second kernel sums in slice order */
 } gemm_plan_t;
 
+/* Counts of one planned call (see gemm_model). Counts are held as doubles (exact
+ * below 2^53). The byte counts follow the no-reuse traffic count of "Reading a
+ * matrix multiply through its tiles" (section "Count the repeated reads"): every
+ * C tile requests its A row panel and B column panel once per K-step, and C is
+ * written once; over actual ranges at partial tiles ("Edge tiles still matter"),
+ * since the kernels load nothing outside the matrices. */
+typedef struct {
+  double flops;            /* 2 M N K, the algorithmic operation count */
+  double executed_flops;   /* multiply-adds x 2 the kernel executes, zero padding of partial
+                              tiles and of the K range included */
+  double bytes_a;          /* bytes of A the load schedule requests: M K ceil(N / tile_n) elements */
+  double bytes_b;          /* bytes of B requested: K N ceil(M / tile_m) elements */
+  double bytes_c;          /* bytes of C written: M N elements */
+  double bytes_workspace;  /* split-K partial tiles written and read back (0 without split-K) */
+  double compulsory_bytes; /* A and B read once, C written once */
+  int64_t tiles;           /* C tiles */
+  int64_t k_steps;         /* K-steps per tile over the whole K range: ceil(K / tile_k) */
+  int64_t footprint_bytes; /* working set of "What fits in local storage?": an A tile and a B tile in
+                              the input format plus the fp32 (int32) C tile */
+  int64_t lds_bytes;       /* LDS per workgroup, all stages */
+} gemm_model_t;
+
 /* Create a handle on the CURRENT HIP device. Host-only: no device work is enqueued.
  * Returns GEMM_ERR_NO_DEVICE if no device is visible, GEMM_ERR_ARCH if the current
  * device is not gfx950, GEMM_ERR_INVALID_ARG if out is NULL. On success *out owns
@@ -179,6 +201,13 @@ gemm_status_t gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const 
 gemm_status_t gemm_plan_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K,
                            const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc,
                            gemm_dtype_t dtype, gemm_plan_t* out);
+
+/* The counts of gemm_model_t for a plan (from gemm_plan / gemm_plan_op, or any
+ * plan_t filled by the caller with kernel 1..4 and positive tile sizes) and the
+ * call's M, N, K and dtype. Host-only. Errors: GEMM_ERR_INVALID_ARG for null
+ * pointers, negative sizes or an inconsistent plan, GEMM_ERR_UNSUPPORTED_DTYPE. */
+gemm_status_t gemm_model(const gemm_plan_t* plan, int64_t M, int64_t N, int64_t K, gemm_dtype_t dtype,
+                         gemm_model_t* out);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* gemm_status_string(gemm_status_t s);

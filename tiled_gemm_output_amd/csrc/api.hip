@@ -375,6 +375,51 @@ gemm_status_t gemm_run_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64
   return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
+gemm_status_t gemm_model(const gemm_plan_t* plan, int64_t M, int64_t N, int64_t K, gemm_dtype_t dtype,
+                         gemm_model_t* out) {
+  if (plan == nullptr || out == nullptr) return GEMM_ERR_INVALID_ARG;
+  const int d = (int)dtype;
+  if (d < GEMM_I32_I32 || d > GEMM_F16_F16) return GEMM_ERR_UNSUPPORTED_DTYPE;
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+  const gemm_plan_t& p = *plan;
+  if (p.kernel < 0 || p.kernel > 4) return GEMM_ERR_INVALID_ARG;
+  gemm_model_t m;
+  std::memset(&m, 0, sizeof(m));
+  const double s_in = d == GEMM_I32_I32 ? 4.0 : 2.0, s_out = (double)out_bytes(d);
+  const double dM = (double)M, dN = (double)N, dK = (double)K;
+  m.flops = 2.0 * dM * dN * dK;
+  m.compulsory_bytes = s_in * (dM * dK + dK * dN) + s_out * dM * dN;
+  if (M > 0 && N > 0) m.bytes_c = s_out * dM * dN;  // the zero fill (K = 0) writes C too
+  if (p.kernel >= 2) {
+    if (p.tile_m <= 0 || p.tile_n <= 0 || p.tile_k <= 0 || p.split_k < 1) return GEMM_ERR_INVALID_ARG;
+    const int64_t tm = cdiv(M, p.tile_m), tn = cdiv(N, p.tile_n), nk = cdiv(K, p.tile_k);
+    m.tiles = tm * tn;
+    m.k_steps = nk;
+    m.bytes_a = s_in * dM * dK * (double)tn;
+    m.bytes_b = s_in * dK * dN * (double)tm;
+    m.footprint_bytes = (int64_t)(s_in * (p.tile_m * p.tile_k + p.tile_k * p.tile_n)) + 4LL * p.tile_m * p.tile_n;
+    m.lds_bytes = p.lds_bytes;
+    const double tile_mn = (double)p.tile_m * p.tile_n * (double)m.tiles;
+    if (p.kernel == 2) {
+      m.executed_flops = 2.0 * tile_mn * dK;  // every thread of a tile runs the actual K range
+    } else if (p.kernel == 3) {
+      m.executed_flops = 2.0 * tile_mn * (double)(nk * p.tile_k);
+    } else {
+      // per K-slice: its K-tiles, plus the zero K-tile prepended when their number is odd
+      const int64_t per = cdiv(nk, p.split_k);
+      double steps = 0;
+      for (int64_t lo = 0; lo < nk; lo += per) {
+        const int64_t n = (nk - lo) < per ? (nk - lo) : per;
+        steps += (double)(n + (n & 1));
+      }
+      m.executed_flops = 2.0 * tile_mn * steps * p.tile_k;
+    }
+    if (p.split_k > 1) m.bytes_workspace = 2.0 * 4.0 * (double)p.split_k * dM * dN;
+  }
+  *out = m;
+  return GEMM_OK;
+}
+
 gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                        const void* B, int64_t ldb, void* C, int64_t ldc, gemm_dtype_t dtype, void* stream) {
   return gemm_run_op(h, GEMM_OP_N, GEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc, dtype, stream);

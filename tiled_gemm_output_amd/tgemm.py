@@ -29,7 +29,7 @@ OUT_BYTES = {I32_I32: 4, F16_F32: 4, BF16_F32: 4, BF16_BF16: 2, F16_F16: 2}
 KERNEL_NAMES = {0: "none", 1: "zero_fill", 2: "int32_valu", 3: "mfma_16x16x32_one_wave", 4: "mfma_macro_tile"}
 
 EXPORTS = ["gemm_create", "gemm_run", "gemm_run_op", "gemm_destroy", "gemm_set_tile", "gemm_set_split_k",
-           "gemm_check_args", "gemm_check_args_op", "gemm_plan", "gemm_plan_op", "gemm_status_string"]
+           "gemm_check_args", "gemm_check_args_op", "gemm_plan", "gemm_plan_op", "gemm_model", "gemm_status_string"]
 
 
 class GemmPlan(ctypes.Structure):
@@ -41,6 +41,16 @@ class GemmPlan(ctypes.Structure):
         d = {name: getattr(self, name) for name, _ in self._fields_}
         d["kernel_name"] = KERNEL_NAMES.get(self.kernel, "?")
         return d
+
+
+class GemmModel(ctypes.Structure):
+    _fields_ = [("flops", ctypes.c_double), ("executed_flops", ctypes.c_double), ("bytes_a", ctypes.c_double),
+                ("bytes_b", ctypes.c_double), ("bytes_c", ctypes.c_double), ("bytes_workspace", ctypes.c_double),
+                ("compulsory_bytes", ctypes.c_double), ("tiles", ctypes.c_int64), ("k_steps", ctypes.c_int64),
+                ("footprint_bytes", ctypes.c_int64), ("lds_bytes", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 class GemmError(RuntimeError):
@@ -81,6 +91,8 @@ def load(path: str = LIBRARY):
     lib.gemm_plan.restype = i32
     lib.gemm_plan_op.argtypes = [vp, i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, ctypes.POINTER(GemmPlan)]
     lib.gemm_plan_op.restype = i32
+    lib.gemm_model.argtypes = [ctypes.POINTER(GemmPlan), i64, i64, i64, i32, ctypes.POINTER(GemmModel)]
+    lib.gemm_model.restype = i32
     lib.gemm_status_string.argtypes = [i32]
     lib.gemm_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -142,6 +154,14 @@ def gemm_plan_op(h, op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, dtype) -> dict:
     check(load().gemm_plan_op(h, int(op_a), int(op_b), M, N, K, A, lda, B, ldb, C, ldc, int(dtype), ctypes.byref(p)),
           "gemm_plan_op")
     return p.as_dict()
+
+
+def gemm_model(plan, M, N, K, dtype) -> dict:
+    """Counts of a plan (a dict from gemm_plan / gemm_plan_op, or the plan fields)."""
+    p = GemmPlan(**{name: int(plan[name]) for name, _ in GemmPlan._fields_})
+    m = GemmModel()
+    check(load().gemm_model(ctypes.byref(p), M, N, K, int(dtype), ctypes.byref(m)), "gemm_model")
+    return m.as_dict()
 
 
 def tensor_args(a, b, c):
