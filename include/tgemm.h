@@ -86,6 +86,9 @@ typedef struct {
   int32_t lds_bytes;              /* LDS per workgroup */
   int32_t split_k;                /* K-slices: 1, or S > 1 when each tile's reduction is cut into S
                                      slices whose fp32 partial tiles a second kernel sums in slice order */
+  int32_t stages;                 /* LDS stages of the K-tile pipeline (macro-tile kernel: 2, or 4 when
+                                     the launch has at most one workgroup per compute unit) */
+  int32_t reserved;               /* 0 */
 } gemm_plan_t;
 
 /* Counts of one planned call (see gemm_model). Counts are held as doubles (exact
@@ -97,7 +100,8 @@ typedef struct {
 typedef struct {
   double flops;            /* 2 M N K, the algorithmic operation count */
   double executed_flops;   /* multiply-adds x 2 the kernel executes, zero padding of partial
-                              tiles and of the K range included */
+                              tiles and of the K range included (each K-slice of the macro-tile
+                              kernel is padded with zero K-tiles to a multiple of plan.stages) */
   double bytes_a;          /* bytes of A the load schedule requests: M K ceil(N / tile_n) elements */
   double bytes_b;          /* bytes of B requested: K N ceil(M / tile_m) elements */
   double bytes_c;          /* bytes of C written: M N elements */

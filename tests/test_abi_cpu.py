@@ -162,6 +162,20 @@ def test_plan_split_k():
         assert plan(*args)["split_k"] == 1, args
 
 
+def test_plan_stages():
+    """4 LDS stages when the launch has at most one workgroup per compute unit (256)
+    and every K-slice has at least 16 K-tiles; 2 otherwise."""
+    assert plan(8192, 8192, 8192, tgemm.BF16_BF16)["stages"] == 2             # 1024 workgroups
+    p = plan(128, 8192, 8192, tgemm.BF16_F32)                                  # 64 tiles x 4 slices of 32 K-tiles
+    assert (p["grid"] * p["split_k"], p["stages"]) == (256, 4)
+    p = plan(1792, 1792, 1096, tgemm.BF16_BF16)                                # 196 tiles, 18 K-tiles (ragged K)
+    assert (p["tile_m"], p["grid"], p["split_k"], p["stages"]) == (128, 196, 1, 4)
+    assert plan(1792, 1792, 900, tgemm.BF16_BF16)["stages"] == 2              # 15 K-tiles: too short
+    assert plan(1792, 1794, 1096, tgemm.BF16_BF16)["stages"] == 2             # N % 8 != 0: element loader
+    assert plan(9, 9, 9, tgemm.I32_I32)["stages"] == 1
+    assert plan(0, 9, 9, tgemm.BF16_F32)["stages"] == 0
+
+
 def test_plan_vector_loads_need_alignment():
     assert plan(1000, 777, 333, tgemm.BF16_F32)["vector_loads"] == 0        # K, N not multiples of 8
     assert plan(256, 256, 256, tgemm.BF16_F32, A=0x10002)["vector_loads"] == 0  # A not 16-byte aligned

@@ -332,3 +332,38 @@ def test_split_k_setting_limits(h, o):
     check_full(h, o, a, b, tgemm.BF16_F32, splits=1)
     # a forced tile with a forced split
     check_full(h, o, a, b, tgemm.BF16_BF16, tile=(128, 128, 64), splits=6)
+
+
+# ---------------------------------------------------------------- 4-stage pipeline
+
+DEEP = [(1792, 1792, 1096), (1000, 1000, 4096), (136, 2056, 4096), (200, 968, 8000)]
+
+
+@pytest.mark.parametrize("shape", DEEP, ids=str)
+def test_deep_pipeline(h, o, shape):
+    """Launches of at most one workgroup per compute unit run the 4-stage twin of
+    the tile (zero K-tiles pad each slice to a multiple of 4, ragged K tails, edge
+    tiles, split-K): random inputs to the accuracy rule, integer-valued inputs bit
+    for bit, in every format and in the transposed forms."""
+    M, N, K = shape
+    for n, dtype in enumerate([tgemm.BF16_BF16, tgemm.F16_F32, tgemm.BF16_F32, tgemm.F16_F16]):
+        p = plan_of(h, M, N, K, dtype)
+        assert p["stages"] == 4, p
+        a, b = inputs.random_case(M, N, K, G.IN_KIND[dtype], seed=K + n)
+        check_full(h, o, a, b, dtype)
+    for kind, dtype in [("bf16", tgemm.BF16_F32), ("f16", tgemm.F16_F16)]:
+        a = inputs.draw((M, K), "small_int", kind, 71)
+        b = inputs.draw((K, N), "small_int", kind, 73)
+        for ops in [(tgemm.OP_N, tgemm.OP_N), (tgemm.OP_N, tgemm.OP_T), (tgemm.OP_T, tgemm.OP_T)]:
+            c, dc = G.run(h, a, b, dtype, op_a=ops[0], op_b=ops[1])
+            assert dc.untouched_outside()
+            assert np.array_equal(c, oracle_ref(o, a, b, dtype).view(G.np_int(tgemm.OUT_BYTES[dtype]))), ops
+
+
+def test_deep_pipeline_forced_tile(h, o):
+    """A forced 128x128 or 64x64 tile also gets the 4-stage pipeline when the launch is small."""
+    for tile in [(128, 128, 64), (64, 64, 64)]:
+        p = plan_of(h, 520, 264, 2000, tgemm.BF16_F32, tile=tile)
+        assert p["stages"] == 4 and (p["tile_m"], p["tile_n"]) == tile[:2]
+        a, b = inputs.random_case(520, 264, 2000, "bf16", seed=tile[0])
+        check_full(h, o, a, b, tgemm.BF16_F32, tile=tile)

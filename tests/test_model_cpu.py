@@ -22,9 +22,9 @@ def auto_plan(M, N, K, dtype):
                            ctypes.c_void_p(1 << 22), max(N, 1), dtype)
 
 
-def forced_plan(tm, tn, tk, kernel=4, split_k=1, lds=0):
+def forced_plan(tm, tn, tk, kernel=4, split_k=1, lds=0, stages=2):
     return {"tile_m": tm, "tile_n": tn, "tile_k": tk, "threads": 64, "vector_loads": 1, "kernel": kernel,
-            "grid": 0, "lds_bytes": lds, "split_k": split_k}
+            "grid": 0, "lds_bytes": lds, "split_k": split_k, "stages": stages}
 
 
 def test_page_values():
@@ -95,6 +95,9 @@ def test_executed_work_and_split_workspace():
     m = tgemm.gemm_model(p, 128, 8192, 8192, tgemm.BF16_F32)
     assert p["split_k"] == 4 and m["bytes_workspace"] == 2 * 4 * 4 * 128 * 8192
     assert m["executed_flops"] == m["flops"]
+    # 4 stages: 18 K-steps padded with 2 zero K-steps to 20
+    m = tgemm.gemm_model(forced_plan(128, 128, 64, stages=4), 1792, 1792, 1096, tgemm.BF16_BF16)
+    assert m["executed_flops"] == 2 * (14 * 128) ** 2 * 64 * 20
     # 7 K-steps in slices of 3, 3, 1 -> each odd slice gets a zero step: 4 + 4 + 2 = 10 steps
     m = tgemm.gemm_model(forced_plan(64, 64, 64, split_k=3), 64, 64, 7 * 64, tgemm.BF16_F32)
     assert m["executed_flops"] == 2 * 64 * 64 * 64 * 10

@@ -36,6 +36,8 @@ bool is_live(const tgemm_handle* h) {
 
 constexpr int64_t kI32Max = 0x7fffffffLL;
 constexpr int kMaxSplits = 64;  // largest K-slice count gemm_set_split_k accepts
+constexpr int64_t kDeepMaxWorkgroups = 256;  // one per compute unit of MI355X
+constexpr int64_t kDeepMinKTiles = 16;       // per K-slice, so the zero K-tiles padding a slice stay few
 constexpr int64_t kMaxRecords = 0x7FFFFFF0LL;  // must match device_common.h
 
 int out_bytes(int dtype) { return (dtype == GEMM_I32_I32 || dtype == GEMM_F16_F32 || dtype == GEMM_BF16_F32) ? 4 : 2; }
@@ -65,9 +67,13 @@ bool vector_ok(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, cons
   return true;
 }
 
-int find_macro(int tm, int tn, int tk) {
-  for (int i = 0; i < tg::kNumMacroShapes; ++i)
-    if (tg::kMacroShapes[i].bm == tm && tg::kMacroShapes[i].bn == tn && tg::kMacroShapes[i].bk == tk) return i;
+// Macro-tile configuration of a tile with the given number of LDS stages (the
+// first one listed), or -1.
+int find_macro(int tm, int tn, int tk, int stages = 2) {
+  for (int i = 0; i < tg::kNumMacroShapes; ++i) {
+    const tg::MacroShape& m = tg::kMacroShapes[i];
+    if (m.bm == tm && m.bn == tn && m.bk == tk && m.stages == stages) return i;
+  }
   return -1;
 }
 
@@ -134,11 +140,14 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
         vector_ok(M, N, K, A, lda, B, ldb, p.tile_m, p.tile_n, p.tile_k, op_a == GEMM_OP_T, op_b == GEMM_OP_T) ? 1 : 0;
   }
   p.split_k = 1;
+  p.stages = p.kernel == 2 ? 1 : 2;
   if (M == 0 || N == 0) {
     p.kernel = 0;
     p.grid = 0;
+    p.stages = 0;
   } else if (K == 0) {
     p.kernel = 1;
+    p.stages = 0;
     p.grid = cdiv(M * N, 256) < 65536 ? cdiv(M * N, 256) : 65536;
   } else {
     p.grid = cdiv(M, p.tile_m) * cdiv(N, p.tile_n);
@@ -162,6 +171,17 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
     }
     if (sk > nk) sk = nk;
     if (sk >= 2) p.split_k = (int32_t)cdiv(nk, cdiv(nk, sk));
+    // Deeper pipeline: when the launch leaves at most one workgroup per compute unit
+    // (so no other workgroup hides a workgroup's memory latency) and each K-slice is
+    // long, the 4-stage twin of the tile keeps three K-tiles of loads in flight.
+    if (p.kernel == 4 && p.vector_loads && p.grid * p.split_k <= kDeepMaxWorkgroups &&
+        cdiv(nk, p.split_k) >= kDeepMinKTiles) {
+      const int deep = find_macro(p.tile_m, p.tile_n, p.tile_k, 4);
+      if (deep >= 0) {
+        p.stages = 4;
+        p.lds_bytes = tg::kMacroShapes[deep].lds;
+      }
+    }
   }
   *out = p;
   return GEMM_OK;
@@ -357,14 +377,14 @@ gemm_status_t gemm_run_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64
       if (p.kernel == 3) {
         e = tg::launch_small(a, in_kind(dtype), out_kind(dtype), p.vector_loads != 0, s, p.grid, ta, tb);
       } else if (splits == 1) {
-        e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k), a, in_kind(dtype), out_kind(dtype),
+        e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k, p.stages), a, in_kind(dtype), out_kind(dtype),
                              p.vector_loads != 0, s, p.grid, 1, ta, tb);
       } else {
         // partial tiles (fp32, dense, ldc = N) into the workspace, then the ordered reduction
         tg::MacroArgs w = a;
         w.C = h->ws;
         w.ldc = N;
-        e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k), w, in_kind(dtype), 0, p.vector_loads != 0, s,
+        e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k, p.stages), w, in_kind(dtype), 0, p.vector_loads != 0, s,
                              p.grid, splits, ta, tb);
         if (e == hipSuccess)
           e = tg::launch_splitk_reduce((const float*)h->ws, splits, C, ldc, (int)M, (int)N, out_kind(dtype), s);
@@ -405,12 +425,14 @@ gemm_status_t gemm_model(const gemm_plan_t* plan, int64_t M, int64_t N, int64_t 
     } else if (p.kernel == 3) {
       m.executed_flops = 2.0 * tile_mn * (double)(nk * p.tile_k);
     } else {
-      // per K-slice: its K-tiles, plus the zero K-tile prepended when their number is odd
+      // per K-slice: its K-tiles, plus the zero K-tiles prepended to make their number
+      // a multiple of the stage count
       const int64_t per = cdiv(nk, p.split_k);
+      const int64_t ns = p.stages > 0 ? p.stages : 2;
       double steps = 0;
       for (int64_t lo = 0; lo < nk; lo += per) {
         const int64_t n = (nk - lo) < per ? (nk - lo) : per;
-        steps += (double)(n + (n & 1));
+        steps += (double)(n + (ns - n % ns) % ns);
       }
       m.executed_flops = 2.0 * tile_mn * steps * p.tile_k;
     }

@@ -72,11 +72,13 @@ hipError_t launch_splitk_reduce(const float* ws, int splits, void* C, int64_t ld
 }
 
 const MacroShape kMacroShapes[kNumMacroShapes] = {
-    {256, 256, 64, Cfg256x256w8::kThreads, Cfg256x256w8::kLds},
-    {256, 128, 64, Cfg256x128::kThreads, Cfg256x128::kLds},
-    {128, 128, 64, Cfg128x128::kThreads, Cfg128x128::kLds},
-    {64, 64, 64, Cfg64x64::kThreads, Cfg64x64::kLds},
-    {256, 256, 64, Cfg256x256w4::kThreads, Cfg256x256w4::kLds},
+    {256, 256, 64, Cfg256x256w8::kThreads, Cfg256x256w8::kLds, Cfg256x256w8::NS},
+    {256, 128, 64, Cfg256x128::kThreads, Cfg256x128::kLds, Cfg256x128::NS},
+    {128, 128, 64, Cfg128x128::kThreads, Cfg128x128::kLds, Cfg128x128::NS},
+    {64, 64, 64, Cfg64x64::kThreads, Cfg64x64::kLds, Cfg64x64::NS},
+    {256, 256, 64, Cfg256x256w4::kThreads, Cfg256x256w4::kLds, Cfg256x256w4::NS},
+    {128, 128, 64, Cfg128x128s4::kThreads, Cfg128x128s4::kLds, Cfg128x128s4::NS},
+    {64, 64, 64, Cfg64x64s4::kThreads, Cfg64x64s4::kLds, Cfg64x64s4::NS},
 };
 
 hipError_t launch_macro_nn(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,

@@ -18,8 +18,10 @@
 // gfx950 design (differs from the pages' one-thread-per-element kernels):
 //  * waves of 64 lanes, each owning a (BM/WM) x (BN/WN) sub-tile computed with
 //    v_mfma_f32_32x32x16_{bf16,f16};
-//  * two LDS stages (double buffering: the loads of step k+1 are in flight while
-//    step k is multiplied), one barrier per step;
+//  * NS LDS stages (2 by default: the loads of step k+1 are in flight while step k
+//    is multiplied; 4 for launches with at most one workgroup per compute unit,
+//    where more loads in flight hide memory latency that other workgroups cannot),
+//    one barrier per step;
 //  * vector path: 16-byte buffer loads straight from global memory into LDS
 //    (buffer_load_dwordx4 ... lds), no register staging; out-of-range lanes use an
 //    offset beyond the buffer and receive zeros;
@@ -36,17 +38,18 @@
 
 namespace tg {
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int NS_ = 2>
 struct MacroCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, NS = NS_;
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kWTM = BM / WM, kWTN = BN / WN;  // wave sub-tile
   static constexpr int kFM = kWTM / 32, kFN = kWTN / 32;  // 32x32 MFMA blocks per wave
   static constexpr int kABytes = BM * BK * 2, kBBytes = BK * BN * 2;
   static constexpr int kSubsteps = BK / 16;
-  static constexpr int kLds = 2 * (kABytes + kBBytes);
+  static constexpr int kLds = NS * (kABytes + kBBytes);
   static_assert(BK == 64, "four 16-deep substeps per K-step");
+  static_assert(NS >= 2 && NS <= 4, "2 to 4 LDS stages");
   static_assert(kFM >= 1 && kFN >= 1 && kWTM % 32 == 0 && kWTN % 32 == 0, "wave tile must be a multiple of 32x32");
   static_assert(kLds <= 160 * 1024, "LDS budget");
 };
@@ -56,6 +59,8 @@ using Cfg256x256w4 = MacroCfg<256, 256, 64, 2, 2>;  // 4 waves, 128 x 128 per wa
 using Cfg256x128 = MacroCfg<256, 128, 64, 4, 2>;
 using Cfg128x128 = MacroCfg<128, 128, 64, 2, 2>;
 using Cfg64x64 = MacroCfg<64, 64, 64, 2, 2>;
+using Cfg128x128s4 = MacroCfg<128, 128, 64, 2, 2, 4>;  // 4 stages: launches of at most one workgroup per CU
+using Cfg64x64s4 = MacroCfg<64, 64, 64, 2, 2, 4>;
 
 // Physical 16-byte chunk of logical chunk c in a K-contiguous row r (8 chunks per
 // row): c ^ swz_a(r). For any 16 consecutive rows starting at a multiple of 16 and
@@ -139,6 +144,19 @@ struct Opnd {
   }
 };
 
+// LDS buffer I of operand TAG (0 = A, 1 = B): one variable per (TAG, I, size), so
+// that every stage is a distinct object. The compiler then knows which stage each
+// direct load writes and waits only for those before a stage is read.
+template <int TAG, int I, int BYTES>
+__device__ __forceinline__ TG_LDS char* lds_stage() {
+  __shared__ __attribute__((aligned(1024))) char buf[BYTES];
+  return (TG_LDS char*)buf;
+}
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding" (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
 // Loads: kLoadElem = guarded element loads staged in registers; kLoadVec = 16-byte
 // direct loads, the last K-tile may be partial; kLoadVecFull = 16-byte direct loads,
 // K is a multiple of BK.
@@ -194,10 +212,8 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   constexpr int kAPer = OA::kPer, kBPer = OB::kPer;
   constexpr int NR = FM * OA::kReads + FN * OB::kReads;  // LDS reads per substep
   constexpr int NM = FM * FN;                            // MFMAs per substep
-  __shared__ __attribute__((aligned(1024))) char sA0[Cfg::kABytes];
-  __shared__ __attribute__((aligned(1024))) char sA1[Cfg::kABytes];
-  __shared__ __attribute__((aligned(1024))) char sB0[Cfg::kBBytes];
-  __shared__ __attribute__((aligned(1024))) char sB1[Cfg::kBBytes];
+  constexpr int NS = Cfg::NS;
+  static_assert(VEC || NS == 2, "the element loader stages one K-tile ahead in registers: two LDS stages");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -341,38 +357,43 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
         for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<IN>(a[i], b[j], acc[i][j]);
   };
 
-  TG_LDS char* pA0 = (TG_LDS char*)sA0;
-  TG_LDS char* pA1 = (TG_LDS char*)sA1;
-  TG_LDS char* pB0 = (TG_LDS char*)sB0;
-  TG_LDS char* pB1 = (TG_LDS char*)sB1;
+  TG_LDS char* pA[NS];
+  TG_LDS char* pB[NS];
+  static_for<0, NS>([&](auto i) {
+    pA[i.value] = lds_stage<0, i.value, Cfg::kABytes>();
+    pB[i.value] = lds_stage<1, i.value, Cfg::kBBytes>();
+  });
 
   // ---------------- main loop ----------------
-  // Two stages; K-tile kt0 + st lives in stage st % 2. Each step multiplies its
+  // NS stages; K-tile kt0 + st lives in stage st % NS. Each step multiplies its
   // stage in four substeps; the reads of substep s+1 are issued among the MFMAs
   // of substep s. The barrier that ends the step sits after the first half of the
   // last substep's MFMAs: once every wave is past it, the stage just consumed is
-  // refilled with K-tile st + 2 and the next stage's first fragments are read,
-  // both covered by the second half of those MFMAs. When the number of K-tiles is
-  // odd, a zero K-tile (index -1) is prepended so that every step is unconditional.
-  const int kt0 = (nk & 1) ? -1 : 0;
-  const int nsteps = nk - kt0;  // even, >= 2
+  // refilled with K-tile st + NS and the next stage's first fragments are read,
+  // both covered by the second half of those MFMAs. Before the barrier each wave
+  // waits until its loads of K-tile st + 1 have landed (those of the NS - 2 later
+  // K-tiles may still be in flight). Zero K-tiles (indices below 0) are prepended
+  // so that the number of steps is a multiple of NS and every step is unconditional.
+  constexpr int PER = kAPer + kBPer;  // direct loads per wave and K-tile
+  const int kt0 = -((NS - nk % NS) % NS);
+  const int nsteps = nk - kt0;  // a multiple of NS, >= NS
   i32x4 fa[FM], fb[FN], ga[FM], gb[FN];
   if constexpr (VEC) {
-    issue_loads(pA0, pB0, kt0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    static_for<0, NS>([&](auto i) { issue_loads(pA[i.value], pB[i.value], kt0 + i.value); });
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (NS - 1)));  // K-tile kt0 landed
   } else {
     fetch_regs(kt0);
-    store_regs(pA0, pB0);
+    store_regs(pA[0], pB[0]);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   }
   barrier_nofence();
-  if constexpr (VEC)
-    issue_loads(pA1, pB1, kt0 + 1);
-  else
-    fetch_regs(kt0 + 1);
-  read_frags(pA0, pB0, 0, fa, fb);
+  if constexpr (!VEC) fetch_regs(kt0 + 1);
+  read_frags(pA[0], pB[0], 0, fa, fb);
 
-  auto step = [&](TG_LDS char* sa, TG_LDS char* sb, TG_LDS char* na, TG_LDS char* nb, int st) {
+  auto step = [&](auto J, int st) {
+    constexpr int cur = decltype(J)::value, nxt = (cur + 1) % NS;
+    TG_LDS char* const sa = pA[cur];
+    TG_LDS char* const sb = pB[cur];
     read_frags(sa, sb, 1, ga, gb);
     mfma_rows(fa, fb, 0, FM);
     interleave<NM, NR, 0>();
@@ -389,26 +410,23 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
     __builtin_amdgcn_sched_barrier(0);
     // the next stage must be complete in every wave before anyone reads it
     if constexpr (VEC) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of K-tile st + 1 landed
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (NS - 2)));  // this wave's loads of K-tile st + 1 landed
     } else {
-      store_regs(na, nb);                  // K-tile st + 1, fetched one step ago
+      store_regs(pA[nxt], pB[nxt]);        // K-tile st + 1, fetched one step ago
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     }
     barrier_nofence();
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (VEC)
-      issue_loads(sa, sb, kt0 + st + 2);  // out of range on the last two steps: zero-length, no traffic
+      issue_loads(sa, sb, kt0 + st + NS);  // beyond the last K-tile: zero-length, no traffic
     else
       fetch_regs(kt0 + st + 2);
-    read_frags(na, nb, 0, fa, fb);
+    read_frags(pA[nxt], pB[nxt], 0, fa, fb);
     mfma_rows(ga, gb, FM / 2, FM);
-    interleave<(FM - FM / 2) * FN, NR, VEC ? kAPer + kBPer : 0>();
+    interleave<(FM - FM / 2) * FN, NR, VEC ? PER : 0>();
     __builtin_amdgcn_sched_barrier(0);
   };
-  for (int st = 0; st < nsteps; st += 2) {
-    step(pA0, pB0, pA1, pB1, st);
-    step(pA1, pB1, pA0, pB0, st + 1);
-  }
+  for (int st = 0; st < nsteps; st += NS) static_for<0, NS>([&](auto J) { step(J, st + J.value); });
   if constexpr (VEC) __builtin_amdgcn_s_waitcnt(0x0F70);  // trailing loads land before LDS is released
 
   // ---------------- epilogue: write the C tile once ----------------
@@ -449,9 +467,10 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
 
 template <class Cfg, int IN, int OUT, bool TA, bool TB>
 static hipError_t launch_cfg(const MacroArgs& a, bool vec, hipStream_t stream, int64_t grid, int splits) {
+  using Cfg2 = MacroCfg<Cfg::BM, Cfg::BN, Cfg::BK, Cfg::WM, Cfg::WN, 2>;  // for the element loader
   const dim3 g((unsigned)grid, (unsigned)splits), b(Cfg::kThreads);
   if (!vec)
-    hipLaunchKernelGGL((macro_tile_kernel<Cfg, IN, OUT, kLoadElem, TA, TB>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((macro_tile_kernel<Cfg2, IN, OUT, kLoadElem, TA, TB>), g, b, 0, stream, a);
   else if (a.K % Cfg::BK == 0)
     hipLaunchKernelGGL((macro_tile_kernel<Cfg, IN, OUT, kLoadVecFull, TA, TB>), g, b, 0, stream, a);
   else
@@ -478,6 +497,8 @@ static hipError_t launch_layout(int shape, const MacroArgs& a, int in, int out, 
     case 2: return launch_dtype<Cfg128x128, TA, TB>(a, in, out, vec, s, grid, splits);
     case 3: return launch_dtype<Cfg64x64, TA, TB>(a, in, out, vec, s, grid, splits);
     case 4: return launch_dtype<Cfg256x256w4, TA, TB>(a, in, out, vec, s, grid, splits);
+    case 5: return launch_dtype<Cfg128x128s4, TA, TB>(a, in, out, vec, s, grid, splits);
+    case 6: return launch_dtype<Cfg64x64s4, TA, TB>(a, in, out, vec, s, grid, splits);
     default: return hipErrorInvalidValue;
   }
 }

@@ -35,7 +35,8 @@ EXPORTS = ["gemm_create", "gemm_run", "gemm_run_op", "gemm_destroy", "gemm_set_t
 class GemmPlan(ctypes.Structure):
     _fields_ = [("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("vector_loads", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int32), ("split_k", ctypes.c_int32)]
+                ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("stages", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         d = {name: getattr(self, name) for name, _ in self._fields_}
@@ -158,7 +159,7 @@ def gemm_plan_op(h, op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, dtype) -> dict:
 
 def gemm_model(plan, M, N, K, dtype) -> dict:
     """Counts of a plan (a dict from gemm_plan / gemm_plan_op, or the plan fields)."""
-    p = GemmPlan(**{name: int(plan[name]) for name, _ in GemmPlan._fields_})
+    p = GemmPlan(**{name: int(plan.get(name, 0)) for name, _ in GemmPlan._fields_})
     m = GemmModel()
     check(load().gemm_model(ctypes.byref(p), M, N, K, int(dtype), ctypes.byref(m)), "gemm_model")
     return m.as_dict()
