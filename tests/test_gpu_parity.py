@@ -367,3 +367,36 @@ def test_deep_pipeline_forced_tile(h, o):
         assert p["stages"] == 4 and (p["tile_m"], p["tile_n"]) == tile[:2]
         a, b = inputs.random_case(520, 264, 2000, "bf16", seed=tile[0])
         check_full(h, o, a, b, tgemm.BF16_F32, tile=tile)
+
+
+# ---------------------------------------------------------------- output rounding edge cases
+
+def test_output_rounding_edge_values(h, o):
+    """One RNE rounding into bf16/f16: products that land exactly halfway between
+    two output values (ties to even), values near the top of the f16 range, and
+    bf16 results in the subnormal range (below 2^-126), against the oracle's
+    exact rounding, element for element."""
+    rng = np.random.default_rng(99)
+    M, N, K = 64, 64, 32
+    # halfway cases: a = 1 + 2^-8 (exact in bf16), b = e_0 + e_1 -> 1 + 2^-8 + 1 + 2^-8 etc.
+    base = (1.0 + rng.integers(0, 128, size=(M, K)) / 128.0).astype(np.float32)
+    base[: M // 2, 1] = 1.0  # these rows sum to a0 + 2^-8: exactly halfway between two bf16 values
+    ones = np.zeros((K, N), dtype=np.float32)
+    ones[0, :] = 1.0
+    ones[1, :] = 2.0 ** -8   # half an ulp of bf16 in [1, 2)
+    for dtype in (tgemm.BF16_BF16, tgemm.F16_F16):
+        kind = "bf16" if dtype == tgemm.BF16_BF16 else "f16"
+        aa = inputs.to_bits(base, kind)
+        bb = inputs.to_bits(ones, kind)
+        c, _ = G.run(h, aa, bb, dtype)
+        ref = oracle_ref(o, aa, bb, dtype).view(np.int16)
+        assert np.array_equal(c.view(np.int16), ref), dtype
+    # large f16 results (sums near 60000) and tiny bf16 results (2^-130 scale)
+    big = inputs.to_bits(rng.uniform(0.5, 1.0, size=(M, K)).astype(np.float32) * 64, "f16")
+    bigb = inputs.to_bits(rng.uniform(0.5, 1.0, size=(K, N)).astype(np.float32) * 30, "f16")
+    c, _ = G.run(h, big, bigb, tgemm.F16_F16)
+    G.compare(c, oracle_ref(o, big, bigb, tgemm.F16_F16).view(np.int16), "f16")
+    tiny = inputs.to_bits((rng.standard_normal((M, K)) * 2.0 ** -70).astype(np.float32), "bf16")
+    tinyb = inputs.to_bits((rng.standard_normal((K, N)) * 2.0 ** -62).astype(np.float32), "bf16")
+    c, _ = G.run(h, tiny, tinyb, tgemm.BF16_BF16)
+    G.compare(c, oracle_ref(o, tiny, tinyb, tgemm.BF16_BF16).view(np.int16), "bf16")

@@ -84,12 +84,10 @@ __device__ __forceinline__ f32x4 mfma16(i32x4 a, i32x4 b, f32x4 acc) {
                                                   0, 0);
 }
 
-// fp32 -> bfloat16 bits, round to nearest even (NaN stays NaN).
+// fp32 -> bfloat16 bits, round to nearest even (hardware conversion,
+// v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // fp32 -> binary16 bits, round to nearest even (hardware conversion).
