@@ -26,7 +26,9 @@
 //    (buffer_load_dwordx4 ... lds), no register staging; out-of-range lanes use an
 //    offset beyond the buffer and receive zeros;
 //  * element path (unaligned pointers/leading dimensions, contiguous extents not a
-//    multiple of 8): guarded 16-bit loads into registers, then 16-byte LDS writes;
+//    multiple of 8): 16-byte loads of whole chunks at 2-byte alignment, guarded
+//    16-bit loads where a chunk crosses the edge, into registers, then 16-byte
+//    LDS writes;
 //  * LDS layouts XOR-swizzled per 16-byte chunk so that the fragment reads
 //    (ds_read_b128 for K-contiguous tiles; ds_read_b64_tr_b16, which also performs
 //    the transpose MFMA needs, for M/N-contiguous tiles) hit distinct banks;
@@ -289,15 +291,24 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   // the matrices and for kt outside [0, nk)), and their 16-byte LDS writes. Lane l
   // of block t reads 8 consecutive elements of one stored row.
   i32x4 a_reg[kAPer], b_reg[kBPer];
+  // A chunk wholly inside the row is one 16-byte load (2-byte aligned: gfx950
+  // compute queues run with unaligned vector memory access); a chunk that crosses
+  // the end of the row, or of the matrix, is loaded element by element.
   auto fetch8 = [](const uint16_t* src, bool row_ok, int col, int cols) {
-    uint32_t w[4];
+    i32x4 v = i32x4{0, 0, 0, 0};
+    if (row_ok && col + 7 < cols) {
+      __builtin_memcpy(&v, src, 16);
+    } else {
+      uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = (row_ok && col + 2 * e < cols) ? src[2 * e] : 0u;
-      const uint32_t hi = (row_ok && col + 2 * e + 1 < cols) ? src[2 * e + 1] : 0u;
-      w[e] = lo | (hi << 16);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = (row_ok && col + 2 * e < cols) ? src[2 * e] : 0u;
+        const uint32_t hi = (row_ok && col + 2 * e + 1 < cols) ? src[2 * e + 1] : 0u;
+        w[e] = lo | (hi << 16);
+      }
+      v = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     }
-    return i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    return v;
   };
   auto fetch_regs = [&](int kt) {
     const bool ok = (unsigned)kt < (unsigned)nk;

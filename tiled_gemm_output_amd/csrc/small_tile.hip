@@ -87,14 +87,18 @@ __global__ __launch_bounds__(64) void small_tile_kernel(MacroArgs p) {
       load_lds_x4(rs, dst, off);
     } else {
       const uint16_t* src = base + (int64_t)sr * ld + sc;
-      uint32_t w[4];
+      if (sr < rows && sc + 7 < cols) {  // whole chunk: one 16-byte load at 2-byte alignment
+        __builtin_memcpy(&reg, src, 16);
+      } else {
+        uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (sr < rows && sc + 2 * e < cols) ? src[2 * e] : 0u;
-        const uint32_t hi = (sr < rows && sc + 2 * e + 1 < cols) ? src[2 * e + 1] : 0u;
-        w[e] = lo | (hi << 16);
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = (sr < rows && sc + 2 * e < cols) ? src[2 * e] : 0u;
+          const uint32_t hi = (sr < rows && sc + 2 * e + 1 < cols) ? src[2 * e + 1] : 0u;
+          w[e] = lo | (hi << 16);
+        }
+        reg = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
       }
-      reg = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     }
   };
   auto load_tile = [&](TG_LDS char* sa, TG_LDS char* sb, int kt) {
