@@ -121,8 +121,8 @@ typedef struct {
 gemm_status_t gemm_create(gemm_handle_t* out);
 
 /* C = A @ B (see the top of this file). Enqueues on `stream` and returns.
- *   M, N, K    >= 0. M == 0 or N == 0: nothing is launched. K == 0: C is filled
- *              with zeros (the empty sum).
+ *   M, N, K    0 .. 2^30. M == 0 or N == 0: nothing is launched. K == 0: C is
+ *              filled with zeros (the empty sum).
  *   A          device pointer, M x K, row stride lda >= max(K, 1) elements.
  *   B          device pointer, K x N, row stride ldb >= max(N, 1) elements.
  *   C          device pointer, M x N, row stride ldc >= max(N, 1) elements.

@@ -61,6 +61,8 @@ def test_valid_args(dtype):
         ({5: None}, tgemm.ERR_INVALID_ARG),          # B null with elements
         ({7: None}, tgemm.ERR_INVALID_ARG),          # C null with elements
         ({0: 2**31}, tgemm.ERR_INVALID_ARG),         # dimension beyond int32
+        ({1: 2**30 + 1, 6: 2**30 + 1, 8: 2**30 + 1}, tgemm.ERR_INVALID_ARG),  # N beyond 2^30
+        ({2: 2**30 + 1, 4: 2**30 + 1}, tgemm.ERR_INVALID_ARG),               # K beyond 2^30
     ],
 )
 def test_bad_args(patch, expected):
@@ -92,6 +94,11 @@ def test_transposed_operand_strides():
                              None) == tgemm.ERR_INVALID_ARG
     # gemm_check_args is the (N, N) case
     assert tgemm.gemm_check_args(*ok_args(), tgemm.BF16_F32) == ck(tgemm.OP_N, tgemm.OP_N, *ok_args(), tgemm.BF16_F32)
+
+
+def test_largest_dimensions_accepted():
+    assert tgemm.gemm_check_args(2**30, 8, 8, NN, 8, NN, 8, NN, 8, tgemm.BF16_F32) == tgemm.OK
+    assert tgemm.gemm_check_args(2**30 + 1, 8, 8, NN, 8, NN, 8, NN, 8, tgemm.BF16_F32) == tgemm.ERR_INVALID_ARG
 
 
 def test_unknown_dtype():

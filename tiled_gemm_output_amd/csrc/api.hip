@@ -35,6 +35,9 @@ bool is_live(const tgemm_handle* h) {
 }
 
 constexpr int64_t kI32Max = 0x7fffffffLL;
+// Largest M, N, K: the kernels index rows, columns and K in 32-bit integers and add
+// up to a tile (and a K-tile) to them, which stays below 2^31 from here.
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int kMaxSplits = 64;  // largest K-slice count gemm_set_split_k accepts
 constexpr int64_t kDeepMaxWorkgroups = 256;  // one per compute unit of MI355X
 constexpr int64_t kDeepMinKTiles = 16;       // per K-slice, so the zero K-tiles padding a slice stay few
@@ -213,7 +216,7 @@ gemm_status_t gemm_check_args_op(gemm_op_t op_a, gemm_op_t op_b, int64_t M, int6
   if ((op_a != GEMM_OP_N && op_a != GEMM_OP_T) || (op_b != GEMM_OP_N && op_b != GEMM_OP_T))
     return GEMM_ERR_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
-  if (M > kI32Max || N > kI32Max || K > kI32Max) return GEMM_ERR_INVALID_ARG;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMM_ERR_INVALID_ARG;
   // row length of each stored matrix: A is M x K (K x M transposed), B is K x N (N x K transposed)
   const int64_t a_len = op_a == GEMM_OP_N ? K : M, b_len = op_b == GEMM_OP_N ? N : K;
   if (lda < max1(a_len) || ldb < max1(b_len) || ldc < max1(N)) return GEMM_ERR_INVALID_ARG;
