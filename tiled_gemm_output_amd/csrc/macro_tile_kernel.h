@@ -209,8 +209,13 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   constexpr bool VEC = LOAD != kLoadElem;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
   constexpr int FM = Cfg::kFM, FN = Cfg::kFN;
-  using OA = Opnd<BM, BK, !TA, Cfg::kWaves>;
-  using OB = Opnd<BN, BK, TB, Cfg::kWaves>;
+  // Direct loads of an 8-wave workgroup are issued by half of its waves, one per
+  // SIMD: a wave waiting to issue a load then leaves the SIMD's matrix core to the
+  // other wave, which only multiplies (all waves do their share of the MFMAs).
+  // Otherwise every wave loads its share of the K-tile.
+  constexpr int LW = (VEC && Cfg::kWaves >= 8) ? Cfg::kWaves / 2 : Cfg::kWaves;  // loading waves
+  using OA = Opnd<BM, BK, !TA, LW>;
+  using OB = Opnd<BN, BK, TB, LW>;
   constexpr int kAPer = OA::kPer, kBPer = OB::kPer;
   constexpr int NR = FM * OA::kReads + FN * OB::kReads;  // LDS reads per substep
   constexpr int NM = FM * FN;                            // MFMAs per substep
@@ -221,6 +226,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+  const int lwave = wave % LW;  // block index base of a loading wave (unused by the others)
 
   int tile_m, tile_n;
   schedule_tile(blockIdx.x, gridDim.x, p.tiles_m, p.group_m, tile_m, tile_n);
@@ -242,25 +248,25 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   if constexpr (VEC) {
 #pragma unroll
     for (int t = 0; t < kAPer; ++t) {
-      const int r = OA::row(wave, t, lane), c = OA::chunk(r, lane);
+      const int r = OA::row(lwave, t, lane), c = OA::chunk(r, lane);
       const bool in = TA ? (row0 + 8 * c < M) : (row0 + r < M);
       a_off[t] = in ? (uint32_t)(((int64_t)r * lda + 8 * c) * 2) : kOutOfRange;
     }
 #pragma unroll
     for (int t = 0; t < kBPer; ++t) {
-      const int r = OB::row(wave, t, lane), c = OB::chunk(r, lane);
+      const int r = OB::row(lwave, t, lane), c = OB::chunk(r, lane);
       const bool in = TB ? (col0 + r < N) : (col0 + 8 * c < N);
       b_off[t] = in ? (uint32_t)(((int64_t)r * ldb + 8 * c) * 2) : kOutOfRange;
     }
   }
   // Origin of K-tile k0 (element offset) in each stored matrix, and the extent of
   // the stored matrix from there on (bytes), for the buffer descriptors.
-  auto a_origin = [&](int k0) { return TA ? (int64_t)k0 * lda + row0 : (int64_t)row0 * lda + k0; };
-  auto b_origin = [&](int k0) { return TB ? (int64_t)col0 * ldb + k0 : (int64_t)k0 * ldb + col0; };
-  auto a_extent = [&](int k0) {
+  auto a_origin = [&](int k0) __attribute__((always_inline)) { return TA ? (int64_t)k0 * lda + row0 : (int64_t)row0 * lda + k0; };
+  auto b_origin = [&](int k0) __attribute__((always_inline)) { return TB ? (int64_t)col0 * ldb + k0 : (int64_t)k0 * ldb + col0; };
+  auto a_extent = [&](int k0) __attribute__((always_inline)) {
     return (TA ? (int64_t)(K - 1 - k0) * lda + (M - row0) : (int64_t)(M - 1 - row0) * lda + (K - k0)) * 2;
   };
-  auto b_extent = [&](int k0) {
+  auto b_extent = [&](int k0) __attribute__((always_inline)) {
     return (TB ? (int64_t)(N - 1 - col0) * ldb + (K - k0) : (int64_t)(K - 1 - k0) * ldb + (N - col0)) * 2;
   };
 
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   // K-tile outside [0, nk) gets a zero-length buffer, so every lane reads zeros and
   // no memory is touched (this keeps the compiler's tracking of which stage each
   // load writes exact, so it adds no waits before reads of the other stage).
-  auto issue_loads = [&](TG_LDS char* sa, TG_LDS char* sb, int kt) {
+  auto issue_loads = [&](TG_LDS char* sa, TG_LDS char* sb, int kt) __attribute__((always_inline)) {
     const bool ok = (unsigned)kt < (unsigned)nk;
     const int k0 = ok ? (kt_base + kt) * BK : 0;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_origin(k0), ok ? a_extent(k0) : 0);
@@ -276,14 +282,14 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
 #pragma unroll
     for (int t = 0; t < kAPer; ++t) {
       uint32_t off = a_off[t];
-      if constexpr (LOAD == kLoadVec) off = (k0 + OA::kpos(wave, t, lane) < K) ? off : kOutOfRange;
-      load_lds_x4(ra, sa + (wave * kAPer + t) * 1024, off);
+      if constexpr (LOAD == kLoadVec) off = (k0 + OA::kpos(lwave, t, lane) < K) ? off : kOutOfRange;
+      load_lds_x4(ra, sa + (lwave * kAPer + t) * 1024, off);
     }
 #pragma unroll
     for (int t = 0; t < kBPer; ++t) {
       uint32_t off = b_off[t];
-      if constexpr (LOAD == kLoadVec) off = (k0 + OB::kpos(wave, t, lane) < K) ? off : kOutOfRange;
-      load_lds_x4(rb, sb + (wave * kBPer + t) * 1024, off);
+      if constexpr (LOAD == kLoadVec) off = (k0 + OB::kpos(lwave, t, lane) < K) ? off : kOutOfRange;
+      load_lds_x4(rb, sb + (lwave * kBPer + t) * 1024, off);
     }
   };
 
@@ -294,7 +300,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   // A chunk wholly inside the row is one 16-byte load (2-byte aligned: gfx950
   // compute queues run with unaligned vector memory access); a chunk that crosses
   // the end of the row, or of the matrix, is loaded element by element.
-  auto fetch8 = [](const uint16_t* src, bool row_ok, int col, int cols) {
+  auto fetch8 = [](const uint16_t* src, bool row_ok, int col, int cols) __attribute__((always_inline)) {
     i32x4 v = i32x4{0, 0, 0, 0};
     if (row_ok && col + 7 < cols) {
       __builtin_memcpy(&v, src, 16);
@@ -310,7 +316,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
     }
     return v;
   };
-  auto fetch_regs = [&](int kt) {
+  auto fetch_regs = [&](int kt) __attribute__((always_inline)) {
     const bool ok = (unsigned)kt < (unsigned)nk;
     const int k0 = (kt_base + kt) * BK;
 #pragma unroll
@@ -330,7 +336,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
       b_reg[t] = fetch8(p.B + (int64_t)sr * ldb + sc, ok && sr < rows, sc, cols);
     }
   };
-  auto store_regs = [&](TG_LDS char* sa, TG_LDS char* sb) {
+  auto store_regs = [&](TG_LDS char* sa, TG_LDS char* sb) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < kAPer; ++t) *(TG_LDS i32x4*)(sa + (wave * kAPer + t) * 1024 + lane * 16) = a_reg[t];
 #pragma unroll
@@ -389,55 +395,70 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   const int kt0 = -((NS - nk % NS) % NS);
   const int nsteps = nk - kt0;  // a multiple of NS, >= NS
   i32x4 fa[FM], fb[FN], ga[FM], gb[FN];
-  if constexpr (VEC) {
-    static_for<0, NS>([&](auto i) { issue_loads(pA[i.value], pB[i.value], kt0 + i.value); });
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (NS - 1)));  // K-tile kt0 landed
-  } else {
-    fetch_regs(kt0);
-    store_regs(pA[0], pB[0]);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  }
-  barrier_nofence();
-  if constexpr (!VEC) fetch_regs(kt0 + 1);
-  read_frags(pA[0], pB[0], 0, fa, fb);
-
-  auto step = [&](auto J, int st) {
-    constexpr int cur = decltype(J)::value, nxt = (cur + 1) % NS;
-    TG_LDS char* const sa = pA[cur];
-    TG_LDS char* const sb = pB[cur];
-    read_frags(sa, sb, 1, ga, gb);
-    mfma_rows(fa, fb, 0, FM);
-    interleave<NM, NR, 0>();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(sa, sb, 2, fa, fb);
-    mfma_rows(ga, gb, 0, FM);
-    interleave<NM, NR, 0>();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(sa, sb, 3, ga, gb);
-    mfma_rows(fa, fb, 0, FM);
-    interleave<NM, NR, 0>();
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_rows(ga, gb, 0, FM / 2);
-    __builtin_amdgcn_sched_barrier(0);
-    // the next stage must be complete in every wave before anyone reads it
+  // The pipeline, for a wave that loads (LOADER) or one that only multiplies; the
+  // two are separate branch-free copies, so the compiler tracks each one's loads
+  // exactly. A multiplying wave waits for nothing but the barriers: each loading
+  // wave has waited for its own loads of a K-tile before it arrives there.
+  auto run = [&](auto ROLE) __attribute__((always_inline)) {
+    constexpr bool LOADER = decltype(ROLE)::value != 0;
     if constexpr (VEC) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (NS - 2)));  // this wave's loads of K-tile st + 1 landed
+      if constexpr (LOADER) {
+        static_for<0, NS>([&](auto i) { issue_loads(pA[i.value], pB[i.value], kt0 + i.value); });
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (NS - 1)));  // K-tile kt0 landed
+      }
     } else {
-      store_regs(pA[nxt], pB[nxt]);        // K-tile st + 1, fetched one step ago
+      fetch_regs(kt0);
+      store_regs(pA[0], pB[0]);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     }
     barrier_nofence();
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (VEC)
-      issue_loads(sa, sb, kt0 + st + NS);  // beyond the last K-tile: zero-length, no traffic
-    else
-      fetch_regs(kt0 + st + 2);
-    read_frags(pA[nxt], pB[nxt], 0, fa, fb);
-    mfma_rows(ga, gb, FM / 2, FM);
-    interleave<(FM - FM / 2) * FN, NR, VEC ? PER : 0>();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  for (int st = 0; st < nsteps; st += NS) static_for<0, NS>([&](auto J) { step(J, st + J.value); });
+    if constexpr (!VEC) fetch_regs(kt0 + 1);
+    read_frags(pA[0], pB[0], 0, fa, fb);
+
+    auto step = [&](auto J, int st) __attribute__((always_inline)) {
+      constexpr int cur = decltype(J)::value, nxt = (cur + 1) % NS;
+      TG_LDS char* const sa = pA[cur];
+      TG_LDS char* const sb = pB[cur];
+      read_frags(sa, sb, 1, ga, gb);
+      mfma_rows(fa, fb, 0, FM);
+      interleave<NM, NR, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(sa, sb, 2, fa, fb);
+      mfma_rows(ga, gb, 0, FM);
+      interleave<NM, NR, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(sa, sb, 3, ga, gb);
+      mfma_rows(fa, fb, 0, FM);
+      interleave<NM, NR, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_rows(ga, gb, 0, FM / 2);
+      __builtin_amdgcn_sched_barrier(0);
+      // the next stage must be complete in every wave before anyone reads it
+      if constexpr (VEC) {
+        if constexpr (LOADER) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (NS - 2)));  // its loads of K-tile st + 1 landed
+      } else {
+        store_regs(pA[nxt], pB[nxt]);        // K-tile st + 1, fetched one step ago
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      }
+      barrier_nofence();
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (VEC && LOADER)
+        issue_loads(sa, sb, kt0 + st + NS);  // beyond the last K-tile: zero-length, no traffic
+      else
+        fetch_regs(kt0 + st + 2);
+      read_frags(pA[nxt], pB[nxt], 0, fa, fb);
+      mfma_rows(ga, gb, FM / 2, FM);
+      interleave<(FM - FM / 2) * FN, NR, (VEC && LOADER) ? PER : 0>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int st = 0; st < nsteps; st += NS) static_for<0, NS>([&](auto J) { step(J, st + J.value); });
+};
+  if constexpr (LW == Cfg::kWaves)
+    run(IC<1>{});
+  else if (wave < LW)
+    run(IC<1>{});
+  else
+    run(IC<0>{});
   if constexpr (VEC) __builtin_amdgcn_s_waitcnt(0x0F70);  // trailing loads land before LDS is released
 
   // ---------------- epilogue: write the C tile once ----------------
