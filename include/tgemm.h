@@ -159,6 +159,25 @@ gemm_status_t gemm_run_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64
                           const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                           gemm_dtype_t dtype, void* stream);
 
+/* Choose the fastest plan for one call's shape by measurement (the pages' Helion
+ * page: the compiler tunes the tile size automatically). Runs every candidate --
+ * each macro tile (256x256, 256x128, 128x128, 64x64) with K-slice counts up to 32,
+ * the 4-stage twins where they apply, and the 16x16x32 tile for outputs of up to
+ * 2^20 elements -- on the caller's buffers on `stream`: one warm-up launch and
+ * `iters` (1..1000) timed launches each, timed with HIP events. BLOCKS until the
+ * stream has run them. C receives the product (every candidate computes it). The
+ * fastest candidate is written to *best and kept in the handle for this shape
+ * (op_a, op_b, M, N, K, dtype and whether 16-byte loads apply): later gemm_run /
+ * gemm_run_op / gemm_plan calls on the handle with that shape use it. A forced tile
+ * or K-slice count (gemm_set_tile, gemm_set_split_k) takes precedence over a tuned
+ * plan; with one set, or for the integer path and empty products, nothing is
+ * measured and *best is the plan gemm_run would use. Arguments as gemm_run_op;
+ * errors: those of gemm_run_op, GEMM_ERR_INVALID_ARG for a bad handle, iters or
+ * best, GEMM_ERR_HIP for a failing event call. */
+gemm_status_t gemm_tune(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                        const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                        gemm_dtype_t dtype, void* stream, int32_t iters, gemm_plan_t* best);
+
 /* Release a handle and its split-K workspace (hipFree waits for work still using it).
  * NULL or an already destroyed handle -> GEMM_ERR_INVALID_ARG. */
 gemm_status_t gemm_destroy(gemm_handle_t h);

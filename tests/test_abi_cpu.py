@@ -118,6 +118,8 @@ def test_null_or_unknown_handle():
     assert tgemm.gemm_destroy(None) == tgemm.ERR_INVALID_ARG
     assert tgemm.gemm_set_tile(None, 16, 16, 32) == tgemm.ERR_INVALID_ARG
     assert tgemm.gemm_set_split_k(None, 2) == tgemm.ERR_INVALID_ARG
+    p = tgemm.GemmPlan()
+    assert tgemm.load().gemm_tune(None, 0, 0, *ok_args(), tgemm.BF16_F32, None, 5, ctypes.byref(p)) == tgemm.ERR_INVALID_ARG
     assert tgemm.gemm_run(None, *ok_args(), tgemm.BF16_BF16, None) == tgemm.ERR_INVALID_ARG
     bogus = ctypes.c_void_p(0xDEADBEEF0)
     assert tgemm.gemm_destroy(bogus) == tgemm.ERR_INVALID_ARG
@@ -152,6 +154,24 @@ def test_plan_auto_tiles():
     assert p["kernel_name"] == "int32_valu"
 
 
+def test_plan_tile_by_rounds_of_workgroups():
+    """With fewer than 256 tiles of 256x256, the tile with the fewest rounds of
+    workgroups times per-round work (scaled by each tile's cost per flop) wins."""
+    def tile(M, N, K):
+        p = plan(M, N, K, tgemm.BF16_BF16)
+        return p["tile_m"], p["tile_n"], p["split_k"], p["stages"]
+    assert tile(3072, 3072, 3072) == (256, 256, 1, 2)   # 144 tiles in one round, not 288 of 256x128 in two
+    assert tile(3584, 3584, 3584) == (256, 256, 1, 2)   # 196 tiles
+    assert tile(3072, 4096, 1024) == (256, 256, 1, 2)
+    assert tile(2560, 2560, 2560)[:2] == (128, 128)     # 100 of 256x256 would leave 156 CUs idle
+    assert tile(1024, 1024, 1024) == (64, 64, 1, 4)     # short K: 256 tiles of 64x64, 16 K-tiles each
+    assert tile(512, 512, 512) == (64, 64, 1, 4)        # 8 K-tiles, a multiple of the 4 stages
+    assert tile(1536, 1536, 1536)[:2] == (128, 128)     # 144 tiles of 128x128
+    assert tile(128, 8192, 8192)[:3] == (128, 128, 4)   # long K: one row of 128x128 tiles reads B once
+    assert tile(64, 4096, 4096)[:3] == (64, 64, 4)
+    assert tile(16384, 1024, 8192)[:2] == (256, 256)    # 256 tiles: a full round
+
+
 def test_plan_split_k():
     # few C tiles and a long K: the reduction is cut into K-slices
     p = plan(128, 8192, 8192, tgemm.BF16_BF16)
@@ -171,7 +191,8 @@ def test_plan_split_k():
 
 def test_plan_stages():
     """4 LDS stages when the launch has at most one workgroup per compute unit (256)
-    and every K-slice has at least 16 K-tiles; 2 otherwise."""
+    and every K-slice has at least 16 K-tiles, or 8 to 15 in a multiple of 4 (no zero
+    padding tile); 2 otherwise."""
     assert plan(8192, 8192, 8192, tgemm.BF16_BF16)["stages"] == 2             # 1024 workgroups
     p = plan(128, 8192, 8192, tgemm.BF16_F32)                                  # 64 tiles x 4 slices of 32 K-tiles
     assert (p["grid"] * p["split_k"], p["stages"]) == (256, 4)

@@ -8,10 +8,33 @@
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <unordered_map>
 #include <unordered_set>
+#include <vector>
 
 #include "launch.h"
 #include "tgemm.h"
+
+// A call's shape as the plan sees it: the key of the tuned-plan cache.
+struct tune_key {
+  int64_t M, N, K;
+  int op_a, op_b, dtype, vec;
+  bool operator==(const tune_key& o) const {
+    return M == o.M && N == o.N && K == o.K && op_a == o.op_a && op_b == o.op_b && dtype == o.dtype && vec == o.vec;
+  }
+};
+struct tune_key_hash {
+  size_t operator()(const tune_key& k) const {
+    uint64_t h = 1469598103934665603ull;
+    const int64_t v[7] = {k.M, k.N, k.K, k.op_a, k.op_b, k.dtype, k.vec};
+    for (int64_t x : v) h = (h ^ (uint64_t)x) * 1099511628211ull;
+    return (size_t)h;
+  }
+};
+// A tuned choice: kernel (3 small tile, 4 macro tile), tile, K-slices, LDS stages.
+struct tune_choice {
+  int kernel, tm, tn, tk, split_k, stages;
+};
 
 struct tgemm_handle {
   int device;
@@ -20,6 +43,7 @@ struct tgemm_handle {
   int splits;       // forced K-slice count, 0 = automatic
   void* ws;         // split-K workspace (device memory owned by the handle), or null
   size_t ws_bytes;  // its size
+  std::unordered_map<tune_key, tune_choice, tune_key_hash> tuned;  // gemm_tune results
 };
 
 namespace {
@@ -40,6 +64,11 @@ constexpr int64_t kI32Max = 0x7fffffffLL;
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int kMaxSplits = 64;  // largest K-slice count gemm_set_split_k accepts
 constexpr int64_t kDeepMaxWorkgroups = 256;  // one per compute unit of MI355X
+constexpr int64_t kSplitMinKTiles = 32;      // automatic split-K only for long reductions (a second kernel costs
+                                             // a few microseconds)
+constexpr int kMaxTuneIters = 1000;                      // timed launches per candidate, at most
+constexpr int64_t kTuneMaxWorkgroups = 8192;             // split candidates beyond this many workgroups are skipped
+constexpr int64_t kTuneSmallTileMaxOutputs = 1 << 20;    // the 16x16x32 tile is tried for outputs up to this size
 constexpr int64_t kDeepMinKTiles = 16;       // per K-slice, so the zero K-tiles padding a slice stay few
 constexpr int64_t kMaxRecords = 0x7FFFFFF0LL;  // must match device_common.h
 
@@ -80,16 +109,63 @@ int find_macro(int tm, int tn, int tk, int stages = 2) {
   return -1;
 }
 
-// Automatic tile: the largest macro tile that still gives the chip (256 CUs) a
-// full wave of workgroups; smaller tiles for smaller problems.
-int auto_macro(int64_t M, int64_t N) {
+// Automatic tile. With at least one full round of 256x256 tiles (256 compute
+// units), the 256x256 tile, which requests the fewest bytes per flop. Otherwise the
+// tile among 256x256, 256x128 and 128x128 with the lowest estimated time: rounds of
+// workgroups x per-CU work per round x the tile's measured cost per unit of work
+// relative to 256x256 (MI355X, bf16: 256x128 1.52; 128x128 1.28 with two workgroups
+// per CU, 1.86 with one). Tile counts that leave a nearly empty last round lose
+// (3072^3: 144 tiles of 256x256 in one round beat 288 of 256x128 in two). Outputs
+// where 128x128 leaves at least half of the chip idle use 64x64: below 128 such tiles
+// when K is short (no split-K follows; 1024^3 runs in half the time on 64x64), below
+// 64 when K is long (split-K then fills the chip, and a 128-row tile reads B once
+// for outputs of at most 128 rows).
+int auto_macro(int64_t M, int64_t N, int64_t K) {
+  constexpr int64_t kCUs = 256;
   const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
-  if (t256 >= 256) return 0;
-  const int64_t t256x128 = cdiv(M, 256) * cdiv(N, 128);
-  if (t256x128 >= 256) return 1;
+  if (t256 >= kCUs || t256 == 0) return 0;  // an empty output launches nothing
+  struct Cand {
+    int shape, bm, bn, occ;  // occ: workgroups that fit on one CU
+    double f1, f2;           // relative cost per unit of work with 1 and with 2+ workgroups per CU
+  };
+  const Cand cands[] = {{0, 256, 256, 1, 1.0, 1.0}, {1, 256, 128, 1, 1.52, 1.52}, {2, 128, 128, 2, 1.86, 1.28}};
+  int best = 0;
+  double best_t = 0.0;
+  for (const Cand& c : cands) {
+    const int64_t tiles = cdiv(M, c.bm) * cdiv(N, c.bn);
+    const int64_t per_cu = cdiv(tiles, kCUs);  // tiles on the busiest CU
+    const int64_t conc = per_cu < c.occ ? per_cu : c.occ;
+    const int64_t rounds = cdiv(per_cu, conc);
+    const double t = (double)rounds * (double)(conc * c.bm * c.bn) * (conc > 1 ? c.f2 : c.f1);
+    if (best_t == 0.0 || t < best_t) {
+      best_t = t;
+      best = c.shape;
+    }
+  }
   const int64_t t128 = cdiv(M, 128) * cdiv(N, 128);
-  if (t128 >= 64) return 2;
-  return 3;
+  if (best == 2 && t128 < (cdiv(K, 64) < kSplitMinKTiles ? 128 : 64)) return 3;
+  return best;
+}
+
+// The plan of a tuned choice (vector_loads kept from the automatic plan: it does
+// not depend on the tile for the tiles the tuner tries).
+void apply_choice(const tune_choice& c, int64_t M, int64_t N, int64_t K, gemm_plan_t* p) {
+  p->kernel = c.kernel;
+  p->tile_m = c.tm;
+  p->tile_n = c.tn;
+  p->tile_k = c.tk;
+  p->split_k = c.split_k;
+  p->stages = c.stages;
+  if (c.kernel == 3) {
+    p->threads = 64;
+    p->lds_bytes = 4096;
+  } else {
+    const tg::MacroShape& s = tg::kMacroShapes[find_macro(c.tm, c.tn, c.tk, c.stages)];
+    p->threads = s.threads;
+    p->lds_bytes = s.lds;
+  }
+  p->grid = cdiv(M, c.tm) * cdiv(N, c.tn);
+  (void)K;
 }
 
 gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, int64_t N, int64_t K, const void* A,
@@ -121,7 +197,7 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
       else if ((shape = find_macro(ftm, ftn, ftk)) < 0)
         return GEMM_ERR_UNSUPPORTED_TILE;
     } else {
-      shape = auto_macro(M, N);
+      shape = auto_macro(M, N, K);
     }
     if (small) {
       p.tile_m = 16;
@@ -166,7 +242,7 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
     if (p.kernel == 4) {
       if (fs > 0) {
         sk = fs;
-      } else if (!forced && p.grid < 128 && nk >= 8) {
+      } else if (!forced && p.grid < 128 && nk >= kSplitMinKTiles) {
         sk = 256 / p.grid;
         if (sk > 16) sk = 16;
         if (sk > nk / 4) sk = nk / 4;
@@ -176,14 +252,22 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
     if (sk >= 2) p.split_k = (int32_t)cdiv(nk, cdiv(nk, sk));
     // Deeper pipeline: when the launch leaves at most one workgroup per compute unit
     // (so no other workgroup hides a workgroup's memory latency) and each K-slice is
-    // long, the 4-stage twin of the tile keeps three K-tiles of loads in flight.
+    // long (or a multiple of 4 K-tiles, so that no zero tile pads it), the 4-stage
+    // twin of the tile keeps three K-tiles of loads in flight.
+    const int64_t nk_slice = cdiv(nk, p.split_k);
     if (p.kernel == 4 && p.vector_loads && p.grid * p.split_k <= kDeepMaxWorkgroups &&
-        cdiv(nk, p.split_k) >= kDeepMinKTiles) {
+        (nk_slice >= kDeepMinKTiles || (nk_slice >= 8 && nk_slice % 4 == 0))) {
       const int deep = find_macro(p.tile_m, p.tile_n, p.tile_k, 4);
       if (deep >= 0) {
         p.stages = 4;
         p.lds_bytes = tg::kMacroShapes[deep].lds;
       }
+    }
+    // A plan chosen by gemm_tune for this shape replaces the automatic choice (a
+    // forced tile or K-slice count replaces both).
+    if (h != nullptr && !forced && h->splits == 0 && (p.kernel == 3 || p.kernel == 4)) {
+      const auto it = h->tuned.find(tune_key{M, N, K, op_a, op_b, dtype, p.vector_loads});
+      if (it != h->tuned.end()) apply_choice(it->second, M, N, K, &p);
     }
   }
   *out = p;
@@ -303,22 +387,14 @@ gemm_status_t gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const 
   return gemm_plan_op(h, GEMM_OP_N, GEMM_OP_N, M, N, K, A, lda, B, ldb, C, ldc, dtype, out);
 }
 
-gemm_status_t gemm_run_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K,
-                          const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
-                          gemm_dtype_t dtype, void* stream) {
-  if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
-  gemm_plan_t p;
-  gemm_status_t st = plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &p);
-  if (st != GEMM_OK) return st;
-  const bool ta = op_a == GEMM_OP_T, tb = op_b == GEMM_OP_T;
-  static const bool log = std::getenv("TGEMM_LOG") != nullptr;
-  if (log)
-    std::fprintf(stderr,
-                 "tgemm: op=%c%c M=%lld N=%lld K=%lld dtype=%d kernel=%d tile=%dx%dx%d threads=%d vec=%d grid=%lld "
-                 "split_k=%d\n",
-                 ta ? 'T' : 'N', tb ? 'T' : 'N', (long long)M, (long long)N, (long long)K, (int)dtype, p.kernel,
-                 p.tile_m, p.tile_n, p.tile_k, p.threads, p.vector_loads, (long long)p.grid, p.split_k);
-  hipStream_t s = (hipStream_t)stream;
+}  // extern "C"
+
+namespace {
+
+// Enqueue the kernels of plan p (arguments already checked).
+gemm_status_t launch_plan(tgemm_handle* h, const gemm_plan_t& p, bool ta, bool tb, int64_t M, int64_t N, int64_t K,
+                          const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int dtype,
+                          hipStream_t s) {
   hipError_t e = hipSuccess;
   switch (p.kernel) {
     case 0: return GEMM_OK;
@@ -396,6 +472,107 @@ gemm_status_t gemm_run_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64
     }
   }
   return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_run_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                          const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                          gemm_dtype_t dtype, void* stream) {
+  if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
+  gemm_plan_t p;
+  gemm_status_t st = plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &p);
+  if (st != GEMM_OK) return st;
+  const bool ta = op_a == GEMM_OP_T, tb = op_b == GEMM_OP_T;
+  static const bool log = std::getenv("TGEMM_LOG") != nullptr;
+  if (log)
+    std::fprintf(stderr,
+                 "tgemm: op=%c%c M=%lld N=%lld K=%lld dtype=%d kernel=%d tile=%dx%dx%d threads=%d vec=%d grid=%lld "
+                 "split_k=%d stages=%d\n",
+                 ta ? 'T' : 'N', tb ? 'T' : 'N', (long long)M, (long long)N, (long long)K, (int)dtype, p.kernel,
+                 p.tile_m, p.tile_n, p.tile_k, p.threads, p.vector_loads, (long long)p.grid, p.split_k, p.stages);
+  return launch_plan(h, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, (hipStream_t)stream);
+}
+
+gemm_status_t gemm_tune(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K,
+                        const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                        gemm_dtype_t dtype, void* stream, int32_t iters, gemm_plan_t* best) {
+  if (!is_live(h) || best == nullptr || iters < 1 || iters > kMaxTuneIters) return GEMM_ERR_INVALID_ARG;
+  gemm_plan_t base;
+  gemm_status_t st = plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &base);
+  if (st != GEMM_OK) return st;
+  // Nothing to choose: forced settings, the integer path, empty products.
+  if (h->tm != 0 || h->splits != 0 || (base.kernel != 3 && base.kernel != 4)) {
+    *best = base;
+    return GEMM_OK;
+  }
+  const tune_key key{M, N, K, (int)op_a, (int)op_b, (int)dtype, base.vector_loads};
+  h->tuned.erase(key);
+  st = plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &base);  // the automatic plan
+  if (st != GEMM_OK) return st;
+  const bool ta = op_a == GEMM_OP_T, tb = op_b == GEMM_OP_T;
+  const bool vec = base.vector_loads != 0;
+
+  // Candidates: every 2-stage macro tile of the 8- and 4-wave kinds with K-slice
+  // counts up to 32 (each slice at least 2 K-tiles), the 4-stage twins where they
+  // apply, and the one-wave 16x16x32 tile for small outputs.
+  std::vector<tune_choice> cand;
+  auto add = [&](const tune_choice& c) {
+    for (const tune_choice& d : cand)
+      if (d.kernel == c.kernel && d.tm == c.tm && d.tn == c.tn && d.split_k == c.split_k && d.stages == c.stages)
+        return;
+    cand.push_back(c);
+  };
+  const int shapes[] = {0, 1, 2, 3};
+  const int split_try[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
+  for (int si : shapes) {
+    const tg::MacroShape& m = tg::kMacroShapes[si];
+    if (vector_ok(M, N, K, A, lda, B, ldb, m.bm, m.bn, m.bk, ta, tb) != vec) continue;  // same loader as the plan
+    const int64_t grid = cdiv(M, m.bm) * cdiv(N, m.bn), nk = cdiv(K, m.bk);
+    for (int sk : split_try) {
+      if (sk > 1 && (nk / sk < 2 || grid * sk > kTuneMaxWorkgroups)) continue;
+      const int eff = sk > 1 ? (int)cdiv(nk, cdiv(nk, sk)) : 1;
+      add(tune_choice{4, m.bm, m.bn, m.bk, eff, 2});
+      if (vec && find_macro(m.bm, m.bn, m.bk, 4) >= 0 && cdiv(nk, eff) >= 4) add(tune_choice{4, m.bm, m.bn, m.bk, eff, 4});
+    }
+  }
+  if (M * N <= kTuneSmallTileMaxOutputs) add(tune_choice{3, 16, 16, 32, 1, 2});
+
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return GEMM_ERR_HIP;
+  }
+  float best_ms = 0.0f;
+  int best_i = -1;
+  for (size_t i = 0; i < cand.size() && st == GEMM_OK; ++i) {
+    gemm_plan_t p = base;
+    apply_choice(cand[i], M, N, K, &p);
+    st = launch_plan(h, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, s);  // warm-up (and workspace)
+    if (st != GEMM_OK) break;
+    if (hipEventRecord(e0, s) != hipSuccess) st = GEMM_ERR_HIP;
+    for (int r = 0; r < iters && st == GEMM_OK; ++r)
+      st = launch_plan(h, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, s);
+    float ms = 0.0f;
+    if (st == GEMM_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                          hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+      st = GEMM_ERR_HIP;
+    if (st == GEMM_OK && (best_i < 0 || ms < best_ms)) {
+      best_ms = ms;
+      best_i = (int)i;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st != GEMM_OK) return st;
+  h->tuned[key] = cand[best_i];
+  gemm_plan_t p = base;
+  apply_choice(cand[best_i], M, N, K, &p);
+  *best = p;
+  return GEMM_OK;
 }
 
 gemm_status_t gemm_model(const gemm_plan_t* plan, int64_t M, int64_t N, int64_t K, gemm_dtype_t dtype,

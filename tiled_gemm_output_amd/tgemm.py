@@ -28,7 +28,7 @@ IN_BYTES = {I32_I32: 4, F16_F32: 2, BF16_F32: 2, BF16_BF16: 2, F16_F16: 2}
 OUT_BYTES = {I32_I32: 4, F16_F32: 4, BF16_F32: 4, BF16_BF16: 2, F16_F16: 2}
 KERNEL_NAMES = {0: "none", 1: "zero_fill", 2: "int32_valu", 3: "mfma_16x16x32_one_wave", 4: "mfma_macro_tile"}
 
-EXPORTS = ["gemm_create", "gemm_run", "gemm_run_op", "gemm_destroy", "gemm_set_tile", "gemm_set_split_k",
+EXPORTS = ["gemm_create", "gemm_run", "gemm_run_op", "gemm_tune", "gemm_destroy", "gemm_set_tile", "gemm_set_split_k",
            "gemm_check_args", "gemm_check_args_op", "gemm_plan", "gemm_plan_op", "gemm_model", "gemm_status_string"]
 
 
@@ -78,6 +78,9 @@ def load(path: str = LIBRARY):
     lib.gemm_run.restype = i32
     lib.gemm_run_op.argtypes = [vp, i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, vp]
     lib.gemm_run_op.restype = i32
+    lib.gemm_tune.argtypes = [vp, i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, vp, i32,
+                              ctypes.POINTER(GemmPlan)]
+    lib.gemm_tune.restype = i32
     lib.gemm_destroy.argtypes = [vp]
     lib.gemm_destroy.restype = i32
     lib.gemm_set_tile.argtypes = [vp, i32, i32, i32]
@@ -134,6 +137,15 @@ def gemm_run(h, M, N, K, A, lda, B, ldb, C, ldc, dtype, stream=None) -> int:
 
 def gemm_run_op(h, op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, dtype, stream=None) -> int:
     return load().gemm_run_op(h, int(op_a), int(op_b), M, N, K, A, lda, B, ldb, C, ldc, int(dtype), stream)
+
+
+def gemm_tune(h, op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, dtype, stream=None, iters: int = 5) -> dict:
+    """Measure the candidate plans for this shape and keep the fastest in the handle
+    (blocks until the timed launches have run); returns that plan."""
+    p = GemmPlan()
+    check(load().gemm_tune(h, int(op_a), int(op_b), M, N, K, A, lda, B, ldb, C, ldc, int(dtype), stream, int(iters),
+                           ctypes.byref(p)), "gemm_tune")
+    return p.as_dict()
 
 
 def gemm_check_args(M, N, K, A, lda, B, ldb, C, ldc, dtype) -> int:
@@ -209,6 +221,12 @@ class Gemm:
 
     def run(self, a, b, c, dtype, stream=None) -> None:
         run_tensors(self.h, a, b, c, dtype, stream)
+
+    def tune(self, a, b, c, dtype, stream=None, iters: int = 5) -> dict:
+        """gemm_tune on row-major tensors (see include/tgemm.h)."""
+        M, N, K, A, lda, B, ldb, C, ldc = tensor_args(a, b, c)
+        s = stream if stream is not None else current_stream()
+        return gemm_tune(self.h, OP_N, OP_N, M, N, K, A, lda, B, ldb, C, ldc, dtype, s, iters)
 
     def close(self) -> None:
         if self.h is not None:
