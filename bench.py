@@ -105,13 +105,19 @@ def cpu_baseline(o, a, b, w, target_s: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # The card's clock settles only after ~100 launches of sustained load (8192^3 runs
+    # ~915 us per launch at first, ~795 us from then on); the default warmup covers that.
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="square8192_bf16")
     ap.add_argument("--tile", default=None, help="force a tile, e.g. 256,256,64")
     ap.add_argument("--split-k", type=int, default=0, help="force the K-slice count (0: the library's choice)")
     ap.add_argument("--op", default="nn", choices=["nn", "nt", "tn", "tt"],
                     help="operand forms: t = that operand is stored transposed (A as K x M, B as N x K)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the K timed steps in one HIP graph and replay it once (for products so small "
+                         "that the host's launch loop, not the GPU, would set the step rate); the time per launch "
+                         "is then the time per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -176,20 +182,40 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     log("bench: warmup done (%d steps), timing %d steps" % (args.warmup, args.steps))
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    per_launch_ms = [s.elapsed_time(e) for s, e in ev]
+    if args.graph:
+        # The launches only enqueue kernels on the given stream (no allocation once the
+        # warm-up has sized any split-K workspace, no memset), so they can be captured.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cs = torch.cuda.current_stream().cuda_stream
+            for _ in range(args.steps):
+                tgemm.check(tgemm.gemm_run_op(h, op_a, op_b, w.M, w.N, w.K, da.data_ptr(), lda, db.data_ptr(), ldb,
+                                              dc.data_ptr(), w.N, dtype, cs), "gemm_run_op (captured)")
+        graph.replay()  # first replay uploads the graph; untimed
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t_start.record(stream)
+        graph.replay()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        total_ms = t_start.elapsed_time(t_end)
+        per_launch_ms = [total_ms / args.steps]
+    else:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t_start.record(stream)
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            step()
+            ev[i][1].record(stream)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        total_ms = t_start.elapsed_time(t_end)
+        per_launch_ms = [s.elapsed_time(e) for s, e in ev]
     ms_per_step = total_ms / args.steps
     launch_ms = float(np.mean(per_launch_ms))
     flops = 2.0 * w.M * w.N * w.K
@@ -230,7 +256,8 @@ def main() -> int:
                    "out": w.out_kind, "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
                    "op": args.op, "kernel": plan["kernel_name"], "grid": plan["grid"], "split_k": plan["split_k"],
                    "threads": plan["threads"],
-                   "vector_loads": plan["vector_loads"], "kernel_source_sha": sha},
+                   "vector_loads": plan["vector_loads"], "kernel_source_sha": sha,
+                   "timing": "hip graph of the timed steps" if args.graph else "hip events around each launch"},
         "pct_of_mfma_peak": 100.0 * value / PEAK_MFMA_16BIT_TFLOPS,
         "launch_us": {"mean": 1e3 * launch_ms, "median": 1e3 * float(np.median(per_launch_ms)),
                       "min": 1e3 * float(np.min(per_launch_ms))},

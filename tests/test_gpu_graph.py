@@ -1,0 +1,87 @@
+"""The library's launches captured in a HIP graph: every replay gives the eager result.
+
+gemm_run only enqueues kernels on the caller's stream (no allocation once a split-K
+workspace exists, no memset), so a caller may capture it. Each case runs eagerly
+first (which also sizes any workspace), captures the same call, and replays the graph
+several times with eager work of the program in between (clearing C, another product
+on the same handle, host synchronisations); every replay must reproduce the eager
+bytes exactly, and the eager result must meet the accuracy rule against the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests import gpu_util as G
+from tiled_gemm_output_amd import inputs, tgemm
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.get()
+
+
+# (M, N, K, dtype, forced tile or None, forced K-slices): the automatic 256x256 plan,
+# a ragged edge-tile plan, split-K with its reduction kernel, the one-wave 16x16x32
+# tile and the int32 path.
+CASES = [
+    (512, 512, 1024, tgemm.BF16_BF16, None, 0),
+    (1000, 777, 333, tgemm.BF16_F32, (64, 64, 64), 0),
+    (128, 2048, 4096, tgemm.BF16_F32, None, 4),
+    (128, 128, 128, tgemm.F16_F32, (16, 16, 32), 0),
+    (96, 80, 70, tgemm.I32_I32, None, 0),
+]
+
+
+def _inputs(M, N, K, dtype, seed):
+    return inputs.random_case(M, N, K, G.IN_KIND[dtype], seed)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "%dx%dx%d-d%d" % c[:4])
+def test_graph_replays_match_eager(o, case):
+    M, N, K, dtype, tile, splits = case
+    print("graph case M=%d N=%d K=%d dtype=%d tile=%s split_k=%d" % (M, N, K, dtype, tile, splits), flush=True)
+    a, b = _inputs(M, N, K, dtype, 7 + M)
+    it = np.int32 if dtype == tgemm.I32_I32 else np.int16
+    da, db = torch.from_numpy(a.view(it)).cuda(), torch.from_numpy(b.view(it)).cuda()
+    ob = tgemm.OUT_BYTES[dtype]
+    dc = torch.zeros((M, N), dtype=G.int_dtype(ob), device="cuda")
+    h = tgemm.gemm_create()
+    try:
+        if tile:
+            tgemm.check(tgemm.gemm_set_tile(h, *tile))
+        tgemm.check(tgemm.gemm_set_split_k(h, splits))
+
+        def call(stream):
+            tgemm.check(tgemm.gemm_run(h, M, N, K, da.data_ptr(), K, db.data_ptr(), N, dc.data_ptr(), N, dtype, stream))
+
+        call(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        eager = dc.cpu().numpy().copy()
+        G.compare(eager, o.gemm(a, b, G.IN_KIND[dtype], G.OUT_KIND[dtype]), G.OUT_KIND[dtype])
+
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call(torch.cuda.current_stream().cuda_stream)
+        # a second product on the same handle between replays (eager work of the program)
+        xa = torch.from_numpy(_inputs(64, 64, 64, dtype, 99)[0].view(it)).cuda()
+        xc = torch.zeros((64, 64), dtype=G.int_dtype(ob), device="cuda")
+        for r in range(4):
+            dc.zero_()
+            tgemm.check(tgemm.gemm_run(h, 64, 64, 64, xa.data_ptr(), 64, xa.data_ptr(), 64, xc.data_ptr(), 64, dtype,
+                                       torch.cuda.current_stream().cuda_stream))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            got = dc.cpu().numpy()
+            assert np.array_equal(got, eager), "replay %d differs from the eager result" % r
+    finally:
+        tgemm.gemm_destroy(h)
