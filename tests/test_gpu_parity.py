@@ -400,3 +400,36 @@ def test_output_rounding_edge_values(h, o):
     tinyb = inputs.to_bits((rng.standard_normal((K, N)) * 2.0 ** -62).astype(np.float32), "bf16")
     c, _ = G.run(h, tiny, tinyb, tgemm.BF16_BF16)
     G.compare(c, oracle_ref(o, tiny, tinyb, tgemm.BF16_BF16).view(np.int16), "bf16")
+
+
+# Regression: at the barrier that ends a K-step, reads of the current stage may still
+# be in flight while the stage's refill is issued. Refills that write zeros at once --
+# a K-tile past the end (a zero-length buffer), the lanes past K of a partial last
+# K-tile -- must wait for them (every wave waits for its LDS reads before such a
+# barrier). Without that wait, one-K-tile split-K slices run after another product
+# (which leaves data in LDS) lost the last substep of a slice in some runs. Each case
+# is repeated with a different product in between; every run must give the same bits,
+# and those must meet the accuracy rule.
+@pytest.mark.parametrize("shape,splits", [((256, 256, 4096), 64), ((256, 256, 4104), 0), ((128, 512, 2056), 8)],
+                         ids=str)
+def test_refill_after_barrier_repeatable(h, o, shape, splits):
+    M, N, K = shape
+    print("refill case M=%d N=%d K=%d splits=%d" % (M, N, K, splits), flush=True)
+    a, b = inputs.random_case(M, N, K, "bf16", seed=97)
+    xa, xb = inputs.random_case(M, N, 2048, "bf16", seed=98)
+    ref = oracle_ref(o, a, b, tgemm.BF16_F32)
+    first = None
+    for r in range(12):
+        check_full(h, o, xa, xb, tgemm.BF16_F32, splits=16)  # leaves other data in every CU's LDS
+        set_tile(h, (64, 64, 64))
+        tgemm.check(tgemm.gemm_set_split_k(h, splits), "gemm_set_split_k")
+        try:
+            c, _ = G.run(h, a, b, tgemm.BF16_F32)
+        finally:
+            set_tile(h, None)
+            tgemm.gemm_set_split_k(h, 0)
+        if first is None:
+            first = c.copy()
+            G.compare(c, ref.view(np.int32), "f32")
+        else:
+            assert np.array_equal(c, first), "run %d differs from the first run" % r

@@ -18,6 +18,7 @@ typedef __attribute__((ext_vector_type(8))) short s16x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 // Element formats of A/B (16-bit floats) and C.
 enum InKind { IN_F16 = 0, IN_BF16 = 1 };
@@ -88,6 +89,14 @@ __device__ __forceinline__ f32x4 mfma16(i32x4 a, i32x4 b, f32x4 acc) {
 // v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two fp32 -> two bfloat16 in one 32-bit word (a in the low half), round to nearest
+// even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // fp32 -> binary16 bits, round to nearest even (hardware conversion).

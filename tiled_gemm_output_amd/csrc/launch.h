@@ -19,6 +19,10 @@ struct MacroArgs {
   // kt_per_split covers all K-tiles and gridDim.y == 1
   int kt_per_split;
   int64_t split_stride;
+  // C's base is 16-byte aligned and ldc a multiple of 4 elements (and so is every
+  // split-K slice): a run of four consecutive elements of a row starting at a
+  // column that is a multiple of 4 can be stored as one aligned 8- or 16-byte word.
+  int c_vec;
 };
 
 struct MacroShape {

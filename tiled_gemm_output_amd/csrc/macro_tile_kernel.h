@@ -365,13 +365,17 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
 #pragma unroll
     for (int i = 1; i < FM; ++i) a[i] = OA::read(sa, a_frag[i], s);
   };
-  // MFMAs of one substep; half 0 = block rows [0, FM/2), half 1 = the rest.
+  // MFMAs of one substep; half 0 = block rows [0, FM/2), half 1 = the rest. The B
+  // fragment goes in the instruction's first operand and the A fragment in its
+  // second: both operands share one lane layout, so this computes the transposed
+  // block, (A B)^T = B^T A^T, which leaves each lane holding runs of four
+  // consecutive columns of one C row (see the epilogue).
   auto mfma_rows = [&](const i32x4(&a)[FM], const i32x4(&b)[FN], int i0, int i1) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
       if (i >= i0 && i < i1)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<IN>(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<IN>(b[j], a[i], acc[i][j]);
   };
 
   TG_LDS char* pA[NS];
@@ -433,9 +437,16 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
       __builtin_amdgcn_sched_barrier(0);
       mfma_rows(ga, gb, 0, FM / 2);
       __builtin_amdgcn_sched_barrier(0);
-      // the next stage must be complete in every wave before anyone reads it
+      // The next stage must be complete in every wave before anyone reads it.
       if constexpr (VEC) {
         if constexpr (LOADER) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (NS - 2)));  // its loads of K-tile st + 1 landed
+        // Right after this barrier the current stage is refilled while reads of it
+        // (the last substep's fragments) may still be in flight. A refill from memory
+        // lands long after they complete, and lanes outside M or N write zeros over
+        // zeros; but a K-tile past the end (a zero-length buffer) and the lanes past K
+        // of a partial last K-tile write their zeros at once, over data still being
+        // read. Before those refills every wave first waits for its LDS reads.
+        if ((kt0 + st + NS) >= nk - (LOAD == kLoadVec ? 1 : 0)) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       } else {
         store_regs(pA[nxt], pB[nxt]);        // K-tile st + 1, fetched one step ago
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -462,32 +473,92 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   if constexpr (VEC) __builtin_amdgcn_s_waitcnt(0x0F70);  // trailing loads land before LDS is released
 
   // ---------------- epilogue: write the C tile once ----------------
-  // acc[i][j][v] holds row 32i + 8*(v/4) + 4*(lane/32) + v%4, column 32j + lane%32
-  // of the wave tile. Interior tiles store without bounds checks; edge tiles drop
-  // the elements outside C. With split-K, slice y writes its partial tile at
-  // C + y * split_stride.
+  // acc[i][j][v] holds row 32i + lane%32 and columns 32j + 8*(v/4) + 4*(lane/32) +
+  // v%4 of the wave tile: for each g = v/4, four consecutive columns of one row. With
+  // split-K, slice y writes its partial tile at C + y * split_stride.
   const int64_t ldc = p.ldc;
   char* const Cout = (char*)p.C + (int64_t)blockIdx.y * p.split_stride * (OUT == OUT_F32 ? 4 : 2);
-  const bool interior = row0 + BM <= M && col0 + BN <= N;
+  constexpr int SO = OUT == OUT_F32 ? 4 : 2;  // bytes per output element
+  if (p.c_vec && row0 + BM <= M && col0 + BN <= N) {
+    // Interior tile, aligned C: each block row (32 rows of the wave tile) goes through
+    // a private LDS slice of the stage memory, written as runs of four elements and
+    // read back as 16-byte chunks along the rows, so that every global store writes
+    // whole 16-byte chunks of consecutive columns (CH lanes per row of the wave
+    // tile). 16-byte chunks are XOR-swizzled by row within the slice.
+    constexpr int RB = Cfg::kWTN * SO;  // bytes per row of a wave tile
+    constexpr int CH = RB / 16;         // 16-byte chunks per row
+    constexpr int SLICE = 32 * RB;      // one block row
+    constexpr int PER_OBJ = Cfg::kABytes / SLICE;
+    static_assert(CH >= 2 && 64 % CH == 0 && PER_OBJ >= 1 && Cfg::kWaves <= NS * PER_OBJ,
+                  "the wave slices fit in the A stages");
+    // every wave is done with the stages, and no direct load is still landing
+    __builtin_amdgcn_s_waitcnt(0);
+    barrier_nofence();
+    TG_LDS char* slice = pA[0];
+    static_for<0, NS>([&](auto S) {
+      if (wave / PER_OBJ == S.value) slice = pA[S.value] + (wave % PER_OBJ) * SLICE;
+    });
+    const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int rb = row0 + wm * Cfg::kWTM + 32 * i + 4 * (lane >> 5);
-      const int col = col0 + wn * Cfg::kWTN + 32 * j + (lane & 31);
-      const int64_t base = (int64_t)rb * ldc + col;
+      for (int j = 0; j < FN; ++j) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int dr = 8 * (v >> 2) + (v & 3);
-        if (interior || (rb + dr < M && col < N)) {
-          const int64_t off = base + (int64_t)dr * ldc;
-          const float x = acc[i][j][v];
-          if constexpr (OUT == OUT_F32)
-            ((float*)Cout)[off] = x;
-          else if constexpr (OUT == OUT_BF16)
-            ((uint16_t*)Cout)[off] = f32_to_bf16_rne(x);
-          else
-            ((uint16_t*)Cout)[off] = f32_to_f16_rne(x);
+        for (int g = 0; g < 4; ++g) {
+          const float x0 = acc[i][j][4 * g], x1 = acc[i][j][4 * g + 1], x2 = acc[i][j][4 * g + 2],
+                      x3 = acc[i][j][4 * g + 3];
+          const int col = 32 * j + 8 * g + 4 * h;  // first of the four columns in the wave tile
+          const int byte = col * SO;
+          const int c = byte >> 4;
+          const uint32_t at = (uint32_t)(r * RB + ((c ^ (r % CH)) << 4) + (byte & 15));
+          if constexpr (OUT == OUT_F32) {
+            *(TG_LDS f32x4*)(slice + at) = f32x4{x0, x1, x2, x3};
+          } else {
+            uint32_t lo, hi;
+            if constexpr (OUT == OUT_BF16) {
+              lo = pack_bf16x2(x0, x1);
+              hi = pack_bf16x2(x2, x3);
+            } else {
+              lo = (uint32_t)f32_to_f16_rne(x0) | ((uint32_t)f32_to_f16_rne(x1) << 16);
+              hi = (uint32_t)f32_to_f16_rne(x2) | ((uint32_t)f32_to_f16_rne(x3) << 16);
+            }
+            *(TG_LDS u32x2*)(slice + at) = u32x2{lo, hi};
+          }
+        }
+      }
+      asm volatile("" ::: "memory");  // the reads below see this wave's writes (LDS is in order per wave)
+      constexpr int ROWS = 64 / CH;  // rows per 64-lane read
+      const int64_t gr0 = (int64_t)(row0 + wm * Cfg::kWTM + 32 * i);
+      const int gc0 = col0 + wn * Cfg::kWTN;
+#pragma unroll
+      for (int q = 0; q < 32 / ROWS; ++q) {
+        const int rr = q * ROWS + lane / CH, c = lane % CH;
+        const i32x4 v = *(TG_LDS i32x4*)(slice + rr * RB + ((c ^ (rr % CH)) << 4));
+        *(i32x4*)(Cout + ((gr0 + rr) * ldc + gc0) * SO + 16 * c) = v;
+      }
+      asm volatile("" ::: "memory");  // the next block row's writes come after these reads
+    }
+  } else {
+    // Edge tile or unaligned C: element by element, dropping what lies outside C.
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = row0 + wm * Cfg::kWTM + 32 * i + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int cb = col0 + wn * Cfg::kWTN + 32 * j + 4 * (lane >> 5);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int col = cb + 8 * (v >> 2) + (v & 3);
+          if (row < M && col < N) {
+            const int64_t off = (int64_t)row * ldc + col;
+            const float x = acc[i][j][v];
+            if constexpr (OUT == OUT_F32)
+              ((float*)Cout)[off] = x;
+            else if constexpr (OUT == OUT_BF16)
+              ((uint16_t*)Cout)[off] = f32_to_bf16_rne(x);
+            else
+              ((uint16_t*)Cout)[off] = f32_to_f16_rne(x);
+          }
         }
       }
     }
