@@ -139,7 +139,12 @@ gemm_status_t gemm_create(gemm_handle_t* out);
  * (the old one is freed, which waits for work still using it), freed by
  * gemm_destroy. Calls on one handle that use split-K share that workspace, so they
  * must be ordered (one stream, or synchronized between streams). The partial sums
- * are added in a fixed order, so results are reproducible run to run. */
+ * are added in a fixed order, so results are reproducible run to run.
+ * Stream capture: a call only enqueues kernels on `stream` (no memset, no
+ * synchronization), so it may be captured into a HIP graph, provided the handle's
+ * workspace is already large enough: a captured call that would have to allocate or
+ * grow it fails (GEMM_ERR_OUT_OF_MEMORY or GEMM_ERR_HIP). Run the call once outside
+ * the capture first. */
 gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                        const void* B, int64_t ldb, void* C, int64_t ldc, gemm_dtype_t dtype, void* stream);
 

@@ -433,3 +433,17 @@ def test_refill_after_barrier_repeatable(h, o, shape, splits):
             G.compare(c, ref.view(np.int32), "f32")
         else:
             assert np.array_equal(c, first), "run %d differs from the first run" % r
+
+
+# Interior tiles are stored as 16-byte chunks staged through LDS when C's base and
+# row stride in bytes are multiples of 16, element by element otherwise; both paths
+# must give the oracle's result and leave everything outside C untouched.
+@pytest.mark.parametrize("dtype,ldc_pad,c_off", [
+    (tgemm.BF16_BF16, 0, 0), (tgemm.BF16_BF16, 4, 0), (tgemm.BF16_BF16, 8, 0), (tgemm.BF16_BF16, 0, 1),
+    (tgemm.BF16_BF16, 0, 8), (tgemm.BF16_F32, 0, 0), (tgemm.BF16_F32, 1, 0), (tgemm.BF16_F32, 4, 0),
+    (tgemm.BF16_F32, 0, 2), (tgemm.F16_F16, 0, 0), (tgemm.F16_F16, 4, 0)], ids=str)
+@pytest.mark.parametrize("tile", [None, (128, 128, 64), (64, 64, 64)], ids=str)
+def test_store_paths(h, o, dtype, ldc_pad, c_off, tile):
+    M, N, K = 512, 512, 192
+    a, b = inputs.random_case(M, N, K, G.IN_KIND[dtype], seed=71 + ldc_pad + c_off)
+    check_full(h, o, a, b, dtype, tile=tile, ldc=N + ldc_pad, offs=(0, 0, c_off))

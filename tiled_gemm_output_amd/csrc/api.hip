@@ -453,7 +453,7 @@ gemm_status_t launch_plan(tgemm_handle* h, const gemm_plan_t& p, bool ta, bool t
       const int64_t nk = cdiv(K, p.tile_k);
       a.kt_per_split = (int)cdiv(nk, splits);
       a.split_stride = (int64_t)M * N;
-      a.c_vec = ((uintptr_t)C & 15) == 0 && ldc % 4 == 0;
+      a.c_vec = ((uintptr_t)C & 15) == 0 && (ldc * out_bytes(dtype)) % 16 == 0;
       if (p.kernel == 3) {
         e = tg::launch_small(a, in_kind(dtype), out_kind(dtype), p.vector_loads != 0, s, p.grid, ta, tb);
       } else if (splits == 1) {
@@ -464,7 +464,7 @@ gemm_status_t launch_plan(tgemm_handle* h, const gemm_plan_t& p, bool ta, bool t
         tg::MacroArgs w = a;
         w.C = h->ws;
         w.ldc = N;
-        w.c_vec = N % 4 == 0;  // hipMalloc'ed workspace: 256-byte aligned, dense slices of M x N
+        w.c_vec = N % 4 == 0;  // hipMalloc'ed workspace: 256-byte aligned, dense fp32 slices of M x N
         e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k, p.stages), w, in_kind(dtype), 0, p.vector_loads != 0, s,
                              p.grid, splits, ta, tb);
         if (e == hipSuccess)

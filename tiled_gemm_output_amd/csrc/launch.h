@@ -19,9 +19,8 @@ struct MacroArgs {
   // kt_per_split covers all K-tiles and gridDim.y == 1
   int kt_per_split;
   int64_t split_stride;
-  // C's base is 16-byte aligned and ldc a multiple of 4 elements (and so is every
-  // split-K slice): a run of four consecutive elements of a row starting at a
-  // column that is a multiple of 4 can be stored as one aligned 8- or 16-byte word.
+  // C's base and row stride in bytes are multiples of 16 (and so is every split-K
+  // slice): interior tiles are stored as aligned 16-byte chunks of consecutive columns.
   int c_vec;
 };
 
