@@ -484,7 +484,10 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
     // a private LDS slice of the stage memory, written as runs of four elements and
     // read back as 16-byte chunks along the rows, so that every global store writes
     // whole 16-byte chunks of consecutive columns (CH lanes per row of the wave
-    // tile). 16-byte chunks are XOR-swizzled by row within the slice.
+    // tile). 16-byte chunks are XOR-swizzled by row within the slice; with 16-bit
+    // outputs a lane writes half a chunk, and the halves are also swapped on rows
+    // with bit 3 set, so that 16 consecutive rows write 16 distinct 8-byte slots of
+    // a 128-byte bank window (the read-back swaps them again).
     constexpr int RB = Cfg::kWTN * SO;  // bytes per row of a wave tile
     constexpr int CH = RB / 16;         // 16-byte chunks per row
     constexpr int SLICE = 32 * RB;      // one block row
@@ -510,7 +513,8 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
           const int col = 32 * j + 8 * g + 4 * h;  // first of the four columns in the wave tile
           const int byte = col * SO;
           const int c = byte >> 4;
-          const uint32_t at = (uint32_t)(r * RB + ((c ^ (r % CH)) << 4) + (byte & 15));
+          const int half = SO == 2 ? ((byte >> 3) & 1) ^ ((r >> 3) & 1) : 0;
+          const uint32_t at = (uint32_t)(r * RB + ((c ^ (r % CH)) << 4) + 8 * half);
           if constexpr (OUT == OUT_F32) {
             *(TG_LDS f32x4*)(slice + at) = f32x4{x0, x1, x2, x3};
           } else {
@@ -533,7 +537,8 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
 #pragma unroll
       for (int q = 0; q < 32 / ROWS; ++q) {
         const int rr = q * ROWS + lane / CH, c = lane % CH;
-        const i32x4 v = *(TG_LDS i32x4*)(slice + rr * RB + ((c ^ (rr % CH)) << 4));
+        i32x4 v = *(TG_LDS i32x4*)(slice + rr * RB + ((c ^ (rr % CH)) << 4));
+        if (SO == 2 && ((rr >> 3) & 1)) v = i32x4{v.z, v.w, v.x, v.y};
         *(i32x4*)(Cout + ((gr0 + rr) * ldc + gc0) * SO + 16 * c) = v;
       }
       asm volatile("" ::: "memory");  // the next block row's writes come after these reads
