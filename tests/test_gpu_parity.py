@@ -447,3 +447,39 @@ def test_store_paths(h, o, dtype, ldc_pad, c_off, tile):
     M, N, K = 512, 512, 192
     a, b = inputs.random_case(M, N, K, G.IN_KIND[dtype], seed=71 + ldc_pad + c_off)
     check_full(h, o, a, b, dtype, tile=tile, ldc=N + ldc_pad, offs=(0, 0, c_off))
+
+
+# Many launches of the same product, every output compared bit for bit with the
+# first (on the device): the kernels are deterministic, so a stage refill landing
+# over a fragment read still in flight (or any other race) would show up as a
+# difference. The first output is also checked against the oracle on sampled rows.
+@pytest.mark.parametrize("name,reps", [("square4096_bf16", 300), ("skinny128x8192x8192_bf16", 1500),
+                                       ("ragged1000x777x333_bf16", 1500)])
+def test_many_launches_identical(h, o, name, reps):
+    torch = pytest.importorskip("torch")
+    w = inputs.WORKLOADS[name]
+    print("repeat case %s x %d" % (name, reps), flush=True)
+    a, b = inputs.make(w)
+    dtype = tgemm.DTYPES[w.dtype]
+    ob = tgemm.OUT_BYTES[dtype]
+    da, db = torch.from_numpy(a.view(np.int16)).cuda(), torch.from_numpy(b.view(np.int16)).cuda()
+    c0 = torch.empty((w.M, w.N), dtype=G.int_dtype(ob), device="cuda")
+    c1 = torch.empty_like(c0)
+    sp = torch.cuda.current_stream().cuda_stream
+
+    def run(c):
+        tgemm.check(tgemm.gemm_run(h, w.M, w.N, w.K, da.data_ptr(), w.K, db.data_ptr(), w.N, c.data_ptr(), w.N,
+                                   dtype, sp), "gemm_run")
+
+    run(c0)
+    bad = torch.zeros((), dtype=torch.int64, device="cuda")
+    for _ in range(reps):
+        c1.fill_(0x55)
+        run(c1)
+        bad += (c1 != c0).any().to(torch.int64)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0, "%d of %d launches differ from the first" % (int(bad.item()), reps)
+    rows, _ = inputs.sample_rows_cols(w.M, w.N, seed=5)
+    got = c0[torch.from_numpy(rows).cuda()].cpu().numpy()
+    ref = o.gemm_rows(a, b, rows, w.in_kind, w.out_kind)
+    G.compare(got, ref.view(G.np_int(ob)), w.out_kind)
