@@ -31,9 +31,10 @@
  *    untouched. No C++ exception crosses this interface.
  *  - C must not overlap A or B (not checked).
  *  - Any alignment of A, B, C and any leading dimension >= the row length is
- *    accepted; a slower element-wise loader is used when 16-byte vector loads are
- *    not possible (they need 16-byte aligned A and B, leading dimensions and the
- *    contiguous extent of each stored operand in multiples of 8 elements).
+ *    accepted. The 16-byte loads straight into LDS need A and B at even byte
+ *    addresses (the 16x16x32 tile also needs 16-byte aligned A and B, leading
+ *    dimensions and contiguous extents in multiples of 8 elements); otherwise a
+ *    slower element-wise loader is used. gemm_plan reports which one applies.
  *  - Operands may also be supplied transposed (gemm_run_op).
  *  - A handle may be used by one host thread at a time.
  */

@@ -79,11 +79,12 @@ class DevMatrix:
 
 
 def run(h, a: np.ndarray, b: np.ndarray, dtype: int, lda=None, ldb=None, ldc=None, offs=(0, 0, 0), stream=None,
-        op_a=tgemm.OP_N, op_b=tgemm.OP_N):
+        op_a=tgemm.OP_N, op_b=tgemm.OP_N, ab_fill=0):
     """Copy A, B to the device with the given layout, run gemm_run (gemm_run_op when an
     operand is to be supplied transposed: then its transpose is what is stored, with
     row stride lda / ldb), return (C host bits, C DevMatrix). a is the M x K op(A),
-    b the K x N op(B)."""
+    b the K x N op(B). ab_fill: bit pattern of the A and B buffers around the matrices
+    (row padding, offsets, guard elements)."""
     torch = _torch()
     M, K = a.shape
     N = b.shape[1]
@@ -94,8 +95,8 @@ def run(h, a: np.ndarray, b: np.ndarray, dtype: int, lda=None, ldb=None, ldc=Non
     lda = sa.shape[1] if lda is None else lda
     ldb = sb.shape[1] if ldb is None else ldb
     ldc = N if ldc is None else ldc
-    da = DevMatrix(sa, sa.shape[0], sa.shape[1], lda, offs[0], ib, fill=0)
-    db = DevMatrix(sb, sb.shape[0], sb.shape[1], ldb, offs[1], ib, fill=0)
+    da = DevMatrix(sa, sa.shape[0], sa.shape[1], lda, offs[0], ib, fill=ab_fill)
+    db = DevMatrix(sb, sb.shape[0], sb.shape[1], ldb, offs[1], ib, fill=ab_fill)
     dc = DevMatrix(None, M, N, ldc, offs[2], ob)
     s = stream if stream is not None else torch.cuda.current_stream()
     if op_a == tgemm.OP_N and op_b == tgemm.OP_N:

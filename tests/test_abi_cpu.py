@@ -199,16 +199,22 @@ def test_plan_stages():
     p = plan(1792, 1792, 1096, tgemm.BF16_BF16)                                # 196 tiles, 18 K-tiles (ragged K)
     assert (p["tile_m"], p["grid"], p["split_k"], p["stages"]) == (128, 196, 1, 4)
     assert plan(1792, 1792, 900, tgemm.BF16_BF16)["stages"] == 2              # 15 K-tiles: too short
-    assert plan(1792, 1794, 1096, tgemm.BF16_BF16)["stages"] == 2             # N % 8 != 0: element loader
+    assert plan(1792, 1794, 1096, tgemm.BF16_BF16)["stages"] == 4             # odd N: still direct loads
+    assert plan(1792, 1792, 1096, tgemm.BF16_BF16, A=0x10001)["stages"] == 2  # odd address: element loader
     assert plan(9, 9, 9, tgemm.I32_I32)["stages"] == 1
     assert plan(0, 9, 9, tgemm.BF16_F32)["stages"] == 0
 
 
 def test_plan_vector_loads_need_alignment():
-    assert plan(1000, 777, 333, tgemm.BF16_F32)["vector_loads"] == 0        # K, N not multiples of 8
-    assert plan(256, 256, 256, tgemm.BF16_F32, A=0x10002)["vector_loads"] == 0  # A not 16-byte aligned
-    assert plan(256, 256, 256, tgemm.BF16_F32, lda=260)["vector_loads"] == 0    # lda not a multiple of 8
-    assert plan(256, 256, 256, tgemm.BF16_F32, lda=264)["vector_loads"] == 1
+    """The macro-tile kernel's direct loads need 2-byte aligned A and B only (whole
+    16-byte chunks at 2-byte alignment; chunks past a row end are dealt with in the
+    kernel); the one-wave 16x16x32 kernel needs 16-byte aligned A, B, strides and
+    contiguous extents."""
+    assert plan(1000, 777, 333, tgemm.BF16_F32)["vector_loads"] == 1        # K, N not multiples of 8
+    assert plan(256, 256, 256, tgemm.BF16_F32, A=0x10002)["vector_loads"] == 1  # A 2-byte aligned
+    assert plan(256, 256, 256, tgemm.BF16_F32, A=0x10001)["vector_loads"] == 0  # A not 2-byte aligned
+    assert plan(256, 256, 256, tgemm.BF16_F32, lda=260)["vector_loads"] == 1
+    assert plan(256, 256, 256, tgemm.BF16_F32, lda=257)["vector_loads"] == 1
 
 
 def plan_op(op_a, op_b, M, N, K, dtype, A=0x10000, lda=None, B=0x20000, ldb=None):
@@ -219,18 +225,14 @@ def plan_op(op_a, op_b, M, N, K, dtype, A=0x10000, lda=None, B=0x20000, ldb=None
 
 
 def test_plan_transposed_vector_loads():
-    """16-byte loads need the contiguous extent of each stored operand in whole
-    8-element chunks: K for A and M for a transposed A; N for B and K for a
-    transposed B."""
+    """Direct loads for every operand form, whatever the extents (the one-wave
+    kernel's strict rule: contiguous extents in whole 8-element chunks -- K for A and
+    M for a transposed A; N for B and K for a transposed B)."""
     T, Nn = tgemm.OP_T, tgemm.OP_N
-    assert plan_op(Nn, T, 8192, 8192, 8192, tgemm.BF16_BF16)["vector_loads"] == 1
-    assert plan_op(T, T, 256, 256, 256, tgemm.BF16_F32)["vector_loads"] == 1
-    assert plan_op(T, Nn, 100, 256, 256, tgemm.BF16_F32)["vector_loads"] == 0  # M % 8 != 0, A transposed
-    assert plan_op(Nn, Nn, 100, 256, 256, tgemm.BF16_F32)["vector_loads"] == 1  # M is not contiguous here
-    assert plan_op(Nn, T, 256, 100, 256, tgemm.BF16_F32)["vector_loads"] == 1   # N % 8 != 0 only matters for B as given
-    assert plan_op(Nn, Nn, 256, 100, 256, tgemm.BF16_F32)["vector_loads"] == 0
-    assert plan_op(Nn, T, 256, 256, 100, tgemm.BF16_F32)["vector_loads"] == 0   # K % 8 != 0, B transposed
-    assert plan_op(T, Nn, 256, 256, 100, tgemm.BF16_F32)["vector_loads"] == 1
+    for op_a, op_b, M, N, K in [(Nn, T, 8192, 8192, 8192), (T, T, 256, 256, 256), (T, Nn, 100, 256, 256),
+                                (Nn, Nn, 100, 256, 256), (Nn, T, 256, 100, 256), (Nn, Nn, 256, 100, 256),
+                                (Nn, T, 256, 256, 100), (T, Nn, 256, 256, 100), (T, T, 99, 101, 103)]:
+        assert plan_op(op_a, op_b, M, N, K, tgemm.BF16_F32)["vector_loads"] == 1, (op_a, op_b, M, N, K)
     # same tile and split choice as the untransposed product
     for op_a in (Nn, T):
         for op_b in (Nn, T):

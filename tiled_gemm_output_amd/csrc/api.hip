@@ -82,15 +82,22 @@ int out_kind(int dtype) {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t max1(int64_t x) { return x > 1 ? x : 1; }
 
-// Can the tile's 16-byte buffer loads be used? Needs 16-byte aligned A and B, row
-// strides and the contiguous extent of each stored operand (K, or M / N for the
-// M/N-contiguous layouts) in whole 8-element chunks, and every in-tile offset below
-// the buffer range limit. ta / tb: A / B supplied transposed.
+// Can the tile's 16-byte buffer loads be used? The macro-tile kernel's direct loads
+// take whole 16-byte chunks at 2-byte alignment and deal with chunks that run past the
+// end of a stored row (relaxed): they need 2-byte aligned A and B. The one-wave
+// 16x16x32 kernel needs 16-byte aligned A and B, row strides and the contiguous extent
+// of each stored operand (K, or M / N for the M/N-contiguous layouts) in whole
+// 8-element chunks (strict). Both need every in-tile offset below the buffer range
+// limit. ta / tb: A / B supplied transposed.
 bool vector_ok(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, int bm, int bn,
-               int bk, bool ta, bool tb) {
-  if (((uintptr_t)A & 15) || ((uintptr_t)B & 15)) return false;
-  if ((lda & 7) || (ldb & 7)) return false;
-  if (((ta ? M : K) & 7) || ((tb ? K : N) & 7)) return false;
+               int bk, bool ta, bool tb, bool relaxed) {
+  if (relaxed) {
+    if (((uintptr_t)A & 1) || ((uintptr_t)B & 1)) return false;
+  } else {
+    if (((uintptr_t)A & 15) || ((uintptr_t)B & 15)) return false;
+    if ((lda & 7) || (ldb & 7)) return false;
+    if (((ta ? M : K) & 7) || ((tb ? K : N) & 7)) return false;
+  }
   // largest in-tile byte offset: (tile rows - 1) * ld + row length of the stored tile
   const int64_t a_rows = ta ? bk : bm, a_len = ta ? bm : bk;
   const int64_t b_rows = tb ? bn : bk, b_len = tb ? bk : bn;
@@ -215,8 +222,10 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
       p.lds_bytes = s.lds;
       p.kernel = 4;
     }
-    p.vector_loads =
-        vector_ok(M, N, K, A, lda, B, ldb, p.tile_m, p.tile_n, p.tile_k, op_a == GEMM_OP_T, op_b == GEMM_OP_T) ? 1 : 0;
+    p.vector_loads = vector_ok(M, N, K, A, lda, B, ldb, p.tile_m, p.tile_n, p.tile_k, op_a == GEMM_OP_T,
+                               op_b == GEMM_OP_T, /*relaxed=*/p.kernel == 4)
+                         ? 1
+                         : 0;
   }
   p.split_k = 1;
   p.stages = p.kernel == 2 ? 1 : 2;
@@ -531,7 +540,7 @@ gemm_status_t gemm_tune(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t
   const int split_try[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
   for (int si : shapes) {
     const tg::MacroShape& m = tg::kMacroShapes[si];
-    if (vector_ok(M, N, K, A, lda, B, ldb, m.bm, m.bn, m.bk, ta, tb) != vec) continue;  // same loader as the plan
+    if (vector_ok(M, N, K, A, lda, B, ldb, m.bm, m.bn, m.bk, ta, tb, true) != vec) continue;  // same loader as the plan
     const int64_t grid = cdiv(M, m.bm) * cdiv(N, m.bn), nk = cdiv(K, m.bk);
     for (int sk : split_try) {
       if (sk > 1 && (nk / sk < 2 || grid * sk > kTuneMaxWorkgroups)) continue;
@@ -540,7 +549,9 @@ gemm_status_t gemm_tune(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t
       if (vec && find_macro(m.bm, m.bn, m.bk, 4) >= 0 && cdiv(nk, eff) >= 4) add(tune_choice{4, m.bm, m.bn, m.bk, eff, 4});
     }
   }
-  if (M * N <= kTuneSmallTileMaxOutputs) add(tune_choice{3, 16, 16, 32, 1, 2});
+  // the 16x16x32 tile, where its (strict) loader choice is the plan's
+  if (M * N <= kTuneSmallTileMaxOutputs && vector_ok(M, N, K, A, lda, B, ldb, 16, 16, 32, ta, tb, false) == vec)
+    add(tune_choice{3, 16, 16, 32, 1, 2});
 
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t e0 = nullptr, e1 = nullptr;

@@ -22,17 +22,20 @@
 //    is multiplied; 4 for launches with at most one workgroup per compute unit,
 //    where more loads in flight hide memory latency that other workgroups cannot),
 //    one barrier per step;
-//  * vector path: 16-byte buffer loads straight from global memory into LDS
-//    (buffer_load_dwordx4 ... lds), no register staging; out-of-range lanes use an
-//    offset beyond the buffer and receive zeros;
-//  * element path (unaligned pointers/leading dimensions, contiguous extents not a
-//    multiple of 8): 16-byte loads of whole chunks at 2-byte alignment, guarded
-//    16-bit loads where a chunk crosses the edge, into registers, then 16-byte
-//    LDS writes;
+//  * vector path (A and B at even addresses: any shape and leading dimension):
+//    16-byte buffer loads straight from global memory into LDS (buffer_load_dwordx4
+//    ... lds), no register staging; out-of-range lanes use an offset beyond the
+//    buffer and receive zeros; chunks that run past the end of a stored row are
+//    cleaned up in LDS once the last K-tile has landed (fix_last);
+//  * element path (an operand at an odd address, or a tile spanning more bytes of
+//    an operand than a buffer range holds): whole 16-byte chunks, guarded 16-bit
+//    loads where a chunk crosses the edge, into registers, then 16-byte LDS writes;
 //  * LDS layouts XOR-swizzled per 16-byte chunk so that the fragment reads
 //    (ds_read_b128 for K-contiguous tiles; ds_read_b64_tr_b16, which also performs
 //    the transpose MFMA needs, for M/N-contiguous tiles) hit distinct banks;
-//  * XCD-aware, grouped workgroup -> tile order (schedule_tile).
+//  * XCD-aware, grouped workgroup -> tile order (schedule_tile);
+//  * the C tile of an interior tile is staged through LDS and stored as 16-byte
+//    chunks along its rows (edge tiles: element stores with bounds checks).
 #pragma once
 
 #include "device_common.h"
@@ -168,6 +171,10 @@ template <int N>
 struct IC {
   static constexpr int value = N;
 };
+template <class T>
+struct TypeIs {
+  using type = T;
+};
 template <int I, int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
@@ -274,6 +281,18 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   // K-tile outside [0, nk) gets a zero-length buffer, so every lane reads zeros and
   // no memory is touched (this keeps the compiler's tracking of which stage each
   // load writes exact, so it adds no waits before reads of the other stage).
+  // Loads are whole 16-byte chunks at 2-byte alignment: a chunk that runs past the
+  // end of a stored row reads the start of the next row (or its padding), which lands
+  // at positions past M or N (outputs that are never stored) or past K (cleared once
+  // the last K-tile has landed, see fix_last). Past the end of the matrix the range
+  // check, which loads a dword only when all four of its bytes are in range, reads
+  // zeros. With an odd stored row length (K for a K-contiguous operand, M or N
+  // otherwise) the dword holding the matrix's last element also covers two bytes past
+  // the end, so that element reads as zero too; it is written into LDS afterwards.
+  const bool a_odd = ((TA ? M : K) & 1) != 0, b_odd = ((TB ? K : N) & 1) != 0;
+  // 1 when the refill of the last K-tile writes zeros at positions that hold data
+  // (a partial K-tile, or the matrix's last element)
+  const int late_zero = (LOAD == kLoadVec || a_odd || b_odd) ? 1 : 0;
   auto issue_loads = [&](TG_LDS char* sa, TG_LDS char* sb, int kt) __attribute__((always_inline)) {
     const bool ok = (unsigned)kt < (unsigned)nk;
     const int k0 = ok ? (kt_base + kt) * BK : 0;
@@ -343,6 +362,52 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
     for (int t = 0; t < kBPer; ++t) *(TG_LDS i32x4*)(sb + (wave * kBPer + t) * 1024 + lane * 16) = b_reg[t];
   };
 
+  // Vector path, the last K-tile of the matrix, once a loading wave's own loads of it
+  // have landed in a stage: in a K-contiguous operand, clear the positions past K of
+  // the chunk that straddles K in each tile row this wave loaded (they hold the next
+  // row's data, possibly not even finite); and where the range check zeroed the
+  // matrix's last element, write it. Then wait until these LDS writes are done.
+  auto fix_operand = [&](auto OT, auto KM, TG_LDS char* st, const uint16_t* base, int64_t ld, int x0, int X, int XT,
+                         int k0) __attribute__((always_inline)) {
+    using O = typename decltype(OT)::type;
+    constexpr bool KMAJ = decltype(KM)::value;
+    if constexpr (KMAJ) {
+      const int kv = K - k0;  // valid reduction indices in this K-tile
+      if (kv & 7) {
+        const int cs = kv >> 3, keep = kv & 7;
+        constexpr int RPW = O::kPer * O::kRowsPerBlock;  // tile rows this wave loaded
+#pragma unroll
+        for (int i0 = 0; i0 < RPW; i0 += 64) {
+          const int i = i0 + lane;
+          if (RPW % 64 == 0 || i < RPW) {
+            const int r = lwave * RPW + i;
+            TG_LDS uint16_t* c = (TG_LDS uint16_t*)(st + r * O::kRow + ((cs ^ O::swz(r)) << 4));
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e >= keep) c[e] = 0;
+            if ((K & 1) && x0 + r == X - 1) c[keep - 1] = base[(int64_t)(X - 1) * ld + (K - 1)];
+          }
+        }
+      }
+    } else {
+      const int kk = K - 1 - k0, xx = X - 1 - x0;  // the matrix's last element in this tile
+      if ((X & 1) && xx >= 0 && xx < XT && lwave == (kk / O::kRowsPerBlock) / O::kPer && lane == 0)
+        *(TG_LDS uint16_t*)(st + kk * O::kRow + (((xx >> 3) ^ O::swz(kk)) << 4) + (xx & 7) * 2) =
+            base[(int64_t)(K - 1) * ld + (X - 1)];
+    }
+  };
+  auto fix_last = [&](TG_LDS char* sa, TG_LDS char* sb, int kt) __attribute__((always_inline)) {
+    // something to do: a K-contiguous operand with K not a multiple of 8, or an
+    // M/N-contiguous operand with an odd row length
+    const bool need = ((!TA || TB) && (K & 7)) || (TA && (M & 1)) || (!TB && (N & 1));
+    if (kt_base + kt == nk_all - 1 && need) {
+      const int k0 = (kt_base + kt) * BK;
+      fix_operand(TypeIs<OA>{}, IC<!TA>{}, sa, p.A, lda, row0, M, BM, k0);
+      fix_operand(TypeIs<OB>{}, IC<TB>{}, sb, p.B, ldb, col0, N, BN, k0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    }
+  };
+
   // ---------------- fragment addressing ----------------
   uint32_t a_frag[FM], b_frag[FN];
 #pragma unroll
@@ -409,6 +474,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
       if constexpr (LOADER) {
         static_for<0, NS>([&](auto i) { issue_loads(pA[i.value], pB[i.value], kt0 + i.value); });
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (NS - 1)));  // K-tile kt0 landed
+        fix_last(pA[0], pB[0], kt0);
       }
     } else {
       fetch_regs(kt0);
@@ -439,14 +505,18 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
       __builtin_amdgcn_sched_barrier(0);
       // The next stage must be complete in every wave before anyone reads it.
       if constexpr (VEC) {
-        if constexpr (LOADER) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (NS - 2)));  // its loads of K-tile st + 1 landed
+        if constexpr (LOADER) {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (NS - 2)));  // its loads of K-tile st + 1 landed
+          fix_last(pA[nxt], pB[nxt], kt0 + st + 1);
+        }
         // Right after this barrier the current stage is refilled while reads of it
         // (the last substep's fragments) may still be in flight. A refill from memory
-        // lands long after they complete, and lanes outside M or N write zeros over
-        // zeros; but a K-tile past the end (a zero-length buffer) and the lanes past K
-        // of a partial last K-tile write their zeros at once, over data still being
-        // read. Before those refills every wave first waits for its LDS reads.
-        if ((kt0 + st + NS) >= nk - (LOAD == kLoadVec ? 1 : 0)) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        // lands long after they complete, and lanes outside M or N write zeros where
+        // only unused data lies; but a K-tile past the end (a zero-length buffer), the
+        // lanes past K of a partial last K-tile and the zeroed last element of the
+        // matrix are written at once, over data still being read. Before those
+        // refills every wave first waits for its LDS reads.
+        if ((kt0 + st + NS) >= nk - late_zero) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       } else {
         store_regs(pA[nxt], pB[nxt]);        // K-tile st + 1, fetched one step ago
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
