@@ -15,6 +15,9 @@ accumulation, bf16 output). Prints ONE JSON line on stdout:
   cpu_baseline the oracle (plain CPU triple loop, binary64 sums) timed on a
                bounded sample of rows of the same product on the host cores
   check        the sampled rows of the GPU result against those oracle rows
+  sclk         the gfx clock under the same load (amd-smi, sampled while the
+               launches continue after the timed region) and the MFMA peak and
+               fraction at that clock
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 """
@@ -60,6 +63,62 @@ def load_traffic(workload: str, sha: str):
     if d.get("kernel_source_sha") != sha:
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def smi_gfx_clock_mhz():
+    """Current gfx clock of GPU 0 from `amd-smi metric -c`, averaged over its XCDs (MHz),
+    and the reported maximum; (None, None) when the tool or its output is not usable."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                           timeout=15)
+        data = json.loads(r.stdout)
+        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+        clocks = gpu["clock"]
+        cur = [v["clk"]["value"] for k, v in clocks.items() if k.startswith("gfx_") and isinstance(v, dict)]
+        top = [v["max_clk"]["value"] for k, v in clocks.items() if k.startswith("gfx_") and isinstance(v, dict)]
+        cur = [float(x) for x in cur if isinstance(x, (int, float))]
+        top = [float(x) for x in top if isinstance(x, (int, float))]
+        if not cur:
+            return None, None
+        return sum(cur) / len(cur), (max(top) if top else None)
+    except Exception:
+        return None, None
+
+
+def sample_clock_under_load(step, seconds: float):
+    """Keep launching ``step`` for ``seconds`` while sampling the gfx clock with amd-smi
+    in a second thread; returns the samples (MHz) and the reported maximum clock."""
+    import threading
+
+    import torch
+
+    samples, top = [], [None]
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            mhz, mx = smi_gfx_clock_mhz()
+            if mhz is None:
+                return
+            samples.append((time.perf_counter(), mhz))
+            top[0] = mx
+
+    th = threading.Thread(target=sampler, daemon=True)
+    t_end = time.perf_counter() + seconds
+    for _ in range(20):
+        step()
+    th.start()
+    while time.perf_counter() < t_end or (th.is_alive() and not samples and time.perf_counter() < t_end + 10):
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    load_end = time.perf_counter()
+    stop.set()
+    th.join(timeout=20)
+    # only readings completed while the launches were still running
+    return [mhz for t, mhz in samples if t <= load_end], top[0]
 
 
 def cpu_threads() -> int:
@@ -121,6 +180,9 @@ def main() -> int:
     # the one-row-per-thread calibration overestimates the per-row cost about twofold:
     # a 22 s target gives about 10-12 s of oracle work
     ap.add_argument("--cpu-seconds", type=float, default=22.0)
+    ap.add_argument("--clock-window", type=float, default=2.0,
+                    help="seconds of further launches after the timed region, during which amd-smi samples "
+                         "the gfx clock (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of 1 GiB (5 times): the known-size kernel whose "
@@ -266,6 +328,23 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": None,
     }
+    props = torch.cuda.get_device_properties(0)
+    result["device"] = {"arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count}
+    result["sclk"] = None
+    if args.clock_window > 0:
+        samples, max_mhz = sample_clock_under_load(step, args.clock_window)
+        if samples:
+            med = float(np.median(samples))
+            top = max_mhz or 2400.0
+            peak_now = PEAK_MFMA_16BIT_TFLOPS * med / top
+            result["sclk"] = {
+                "source": "amd-smi metric -c (gfx clock, mean over XCDs), sampled while the same launches "
+                          "continue for %.1f s after the timed region" % args.clock_window,
+                "median_mhz": med, "min_mhz": float(np.min(samples)), "max_mhz": float(np.max(samples)),
+                "samples": len(samples), "max_clk_mhz": top,
+                "mfma_peak_at_median_tflops": peak_now,
+                "frac_of_peak_at_median": (flops / (launch_ms * 1e-3) / 1e12) / peak_now,
+            }
     if not args.no_cpu_baseline:
         import oracle
 
