@@ -435,9 +435,11 @@ def test_refill_after_barrier_repeatable(h, o, shape, splits):
             assert np.array_equal(c, first), "run %d differs from the first run" % r
 
 
-# Interior tiles are stored as 16-byte chunks staged through LDS when C's base and
-# row stride in bytes are multiples of 16, element by element otherwise; both paths
-# must give the oracle's result and leave everything outside C untouched.
+# Interior tiles are stored as 16-byte chunks staged through LDS, at whatever
+# alignment C's base and row stride give them (2-byte aligned for 16-bit outputs);
+# edge tiles element by element. Every combination must give the oracle's result and
+# leave everything outside C untouched (neighbouring tiles share the 4-byte words
+# and cache lines at their boundary when the row start is not 16-byte aligned).
 @pytest.mark.parametrize("dtype,ldc_pad,c_off", [
     (tgemm.BF16_BF16, 0, 0), (tgemm.BF16_BF16, 4, 0), (tgemm.BF16_BF16, 8, 0), (tgemm.BF16_BF16, 0, 1),
     (tgemm.BF16_BF16, 0, 8), (tgemm.BF16_F32, 0, 0), (tgemm.BF16_F32, 1, 0), (tgemm.BF16_F32, 4, 0),

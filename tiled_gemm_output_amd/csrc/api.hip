@@ -462,7 +462,7 @@ gemm_status_t launch_plan(tgemm_handle* h, const gemm_plan_t& p, bool ta, bool t
       const int64_t nk = cdiv(K, p.tile_k);
       a.kt_per_split = (int)cdiv(nk, splits);
       a.split_stride = (int64_t)M * N;
-      a.c_vec = ((uintptr_t)C & 15) == 0 && (ldc * out_bytes(dtype)) % 16 == 0;
+      a.c_vec = ((uintptr_t)C % (uintptr_t)out_bytes(dtype)) == 0;  // element-aligned C (16-byte stores need no more)
       if (p.kernel == 3) {
         e = tg::launch_small(a, in_kind(dtype), out_kind(dtype), p.vector_loads != 0, s, p.grid, ta, tb);
       } else if (splits == 1) {

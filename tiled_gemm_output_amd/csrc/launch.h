@@ -19,8 +19,9 @@ struct MacroArgs {
   // kt_per_split covers all K-tiles and gridDim.y == 1
   int kt_per_split;
   int64_t split_stride;
-  // C's base and row stride in bytes are multiples of 16 (and so is every split-K
-  // slice): interior tiles are stored as aligned 16-byte chunks of consecutive columns.
+  // C's base is aligned to its element size: interior tiles are stored as 16-byte
+  // chunks of consecutive columns, at whatever alignment the row start gives them
+  // (gfx950 compute queues run with unaligned vector memory access).
   int c_vec;
 };
 

@@ -550,7 +550,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   char* const Cout = (char*)p.C + (int64_t)blockIdx.y * p.split_stride * (OUT == OUT_F32 ? 4 : 2);
   constexpr int SO = OUT == OUT_F32 ? 4 : 2;  // bytes per output element
   if (p.c_vec && row0 + BM <= M && col0 + BN <= N) {
-    // Interior tile, aligned C: each block row (32 rows of the wave tile) goes through
+    // Interior tile: each block row (32 rows of the wave tile) goes through
     // a private LDS slice of the stage memory, written as runs of four elements and
     // read back as 16-byte chunks along the rows, so that every global store writes
     // whole 16-byte chunks of consecutive columns (CH lanes per row of the wave
@@ -609,12 +609,13 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
         const int rr = q * ROWS + lane / CH, c = lane % CH;
         i32x4 v = *(TG_LDS i32x4*)(slice + rr * RB + ((c ^ (rr % CH)) << 4));
         if (SO == 2 && ((rr >> 3) & 1)) v = i32x4{v.z, v.w, v.x, v.y};
-        *(i32x4*)(Cout + ((gr0 + rr) * ldc + gc0) * SO + 16 * c) = v;
+        __builtin_memcpy(Cout + ((gr0 + rr) * ldc + gc0) * SO + 16 * c, &v, 16);  // any element alignment
       }
       asm volatile("" ::: "memory");  // the next block row's writes come after these reads
     }
   } else {
-    // Edge tile or unaligned C: element by element, dropping what lies outside C.
+    // Edge tile (or C not aligned to its element size): element by element, dropping
+    // what lies outside C.
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = row0 + wm * Cfg::kWTM + 32 * i + (lane & 31);
