@@ -319,7 +319,7 @@ def main() -> int:
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.in_kind, "acc": "fp32" if ib == 2 else "i32",
                    "out": w.out_kind, "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
                    "op": args.op, "kernel": plan["kernel_name"], "grid": plan["grid"], "split_k": plan["split_k"],
-                   "threads": plan["threads"],
+                   "tail_split_k": plan["tail_split_k"], "tail_m0": plan["tail_m0"], "threads": plan["threads"],
                    "vector_loads": plan["vector_loads"], "kernel_source_sha": sha,
                    "timing": "hip graph of the timed steps" if args.graph else "hip events around each launch"},
         "pct_of_mfma_peak": 100.0 * value / PEAK_MFMA_16BIT_TFLOPS,

@@ -89,6 +89,11 @@ typedef struct {
                                      slices whose fp32 partial tiles a second kernel sums in slice order */
   int32_t stages;                 /* LDS stages of the K-tile pipeline (macro-tile kernel: 2, or 4 when
                                      the launch has at most one workgroup per compute unit) */
+  int32_t tail_split_k;           /* 0, or S > 1: the tiles of C rows [tail_m0, M) run after the others
+                                     as a second launch of the same tile with S K-slices (fp32 partial
+                                     tiles summed in slice order), so that they fill the compute units
+                                     left idle by a last, partial round of tiles */
+  int32_t tail_m0;                /* first C row of that tail (a multiple of tile_m; 0 without a tail) */
   int32_t reserved;               /* 0 */
 } gemm_plan_t;
 

@@ -205,6 +205,25 @@ def test_plan_stages():
     assert plan(0, 9, 9, tgemm.BF16_F32)["stages"] == 0
 
 
+def test_plan_tail_split():
+    """Automatic 256x256 plans with more than one round of tiles (256, one per compute
+    unit) whose last round is partly full: the tile rows that fill whole rounds run
+    first, then the remaining rows as a second launch with each tile's K range in S
+    slices (S x tail tiles <= 256 workgroups), when the estimate beats one more round."""
+    p = plan(6000, 6000, 6000, tgemm.BF16_BF16)  # 24 x 24 = 576 tiles = 2 rounds + 64
+    # 21 tile rows = 504 tiles in 2 rounds; 3 rows x 24 = 72 tiles x 3 slices = 216 workgroups
+    assert (p["tile_m"], p["grid"], p["split_k"], p["tail_m0"], p["tail_split_k"]) == (256, 576, 1, 21 * 256, 3)
+    p = plan(7000, 7000, 7000, tgemm.BF16_BF16)  # 28 x 28 = 784 = 3 rounds + 16
+    assert (p["tail_m0"], p["tail_split_k"]) == (27 * 256, 9)  # 1 row x 28 tiles x 9 slices = 252
+    p = plan(4352, 4096, 1024, tgemm.BF16_F32)  # 17 x 16 = 272: 16 rows, then 16 tiles x 4 slices
+    assert (p["tail_m0"], p["tail_split_k"]) == (4096, 4)  # 16 K-tiles: at most 16 / 4 slices
+    for shape in [(8192, 8192, 8192), (4096, 4096, 4096), (16384, 1024, 8192), (8191, 8191, 8191),
+                  (4352, 4096, 256),  # 4 K-tiles: too short to split
+                  (2048, 2048, 8192), (128, 8192, 8192)]:
+        p = plan(*shape, tgemm.BF16_BF16)
+        assert (p["tail_split_k"], p["tail_m0"]) == (0, 0), shape
+
+
 def test_plan_vector_loads_need_alignment():
     """The macro-tile kernel's direct loads need 2-byte aligned A and B only (whole
     16-byte chunks at 2-byte alignment; chunks past a row end are dealt with in the

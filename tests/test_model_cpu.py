@@ -112,3 +112,29 @@ def test_model_rejects_bad_plans():
         tgemm.gemm_model(forced_plan(64, 64, 64), -1, 64, 64, tgemm.BF16_F32)
     with pytest.raises(tgemm.GemmError):
         tgemm.gemm_model(forced_plan(64, 64, 64), 64, 64, 64, 7)
+
+
+def test_model_of_a_tail_split():
+    """executed_flops and the workspace of a plan with a split-K tail: the tiles of
+    rows [0, tail_m0) over the whole K range, each tail tile in S slices, each slice
+    (and the whole range) padded with zero K-tiles to a multiple of the stage count."""
+    for M, N, K, dtype in [(6000, 6000, 6000, tgemm.BF16_BF16), (4352, 4096, 1024, tgemm.BF16_F32),
+                           (7000, 7000, 7000, tgemm.F16_F16)]:
+        p = auto_plan(M, N, K, dtype)
+        assert p["tail_split_k"] > 1
+        m = tgemm.gemm_model(p, M, N, K, dtype)
+        tm, tn, tk, S, ns = p["tile_m"], p["tile_n"], p["tile_k"], p["tail_split_k"], p["stages"]
+        nk = -(-K // tk)
+
+        def padded_steps(splits):
+            per = -(-nk // splits)
+            sizes = [min(per, nk - lo) for lo in range(0, nk, per)]
+            return sum(n + (-n) % ns for n in sizes)
+
+        tiles_n = -(-N // tn)
+        main_tiles = (p["tail_m0"] // tm) * tiles_n
+        tail_tiles = (-(-M // tm)) * tiles_n - main_tiles
+        want = 2 * tm * tn * tk * (main_tiles * padded_steps(1) + tail_tiles * padded_steps(S))
+        assert m["executed_flops"] == want
+        assert m["bytes_workspace"] == 8 * S * (M - p["tail_m0"]) * N
+        assert m["flops"] == 2 * M * N * K

@@ -70,6 +70,11 @@ constexpr int kMaxTuneIters = 1000;                      // timed launches per c
 constexpr int64_t kTuneMaxWorkgroups = 8192;             // split candidates beyond this many workgroups are skipped
 constexpr int64_t kTuneSmallTileMaxOutputs = 1 << 20;    // the 16x16x32 tile is tried for outputs up to this size
 constexpr int64_t kDeepMinKTiles = 16;       // per K-slice, so the zero K-tiles padding a slice stay few
+// Cost figures of the tail split (MI355X, bf16): one K-step of a round of 256x256 tiles,
+// and the rate at which the split-K partial tiles are written and read back.
+constexpr double kStepSeconds = 1.55e-6;
+constexpr double kWorkspaceBytesPerSecond = 4.0e12;
+constexpr double kLaunchSeconds = 3.0e-6;
 constexpr int64_t kMaxRecords = 0x7FFFFFF0LL;  // must match device_common.h
 
 int out_bytes(int dtype) { return (dtype == GEMM_I32_I32 || dtype == GEMM_F16_F32 || dtype == GEMM_BF16_F32) ? 4 : 2; }
@@ -154,6 +159,45 @@ int auto_macro(int64_t M, int64_t N, int64_t K) {
   return best;
 }
 
+// Tail split of an automatic 256x256 plan. With more than one round of tiles (one per
+// compute unit), a last round that is only partly full leaves most units idle while
+// its tiles run their whole K range. The last tile rows that do not fit the full
+// rounds can instead run as a second launch with each tile's K range cut into S
+// slices (S x tail tiles <= 256 workgroups, one round of 1/S of the work) plus the
+// ordered reduction. S minimizes the estimate (full rounds + one round of 1/S of the
+// K-steps + the partial tiles' workspace traffic + a launch), taken when it beats one
+// more round by 5%. Returns S (0: no tail) and the tail's first row in *m0.
+int tail_split(int64_t M, int64_t N, int64_t K, int dtype, int64_t* m0) {
+  constexpr int64_t kCUs = 256, T = 256;
+  *m0 = 0;
+  const int64_t tiles_m = cdiv(M, T), tiles_n = cdiv(N, T), tiles = tiles_m * tiles_n;
+  if (tiles <= kCUs || tiles % kCUs == 0) return 0;
+  const int64_t rounds = cdiv(tiles, kCUs);
+  const int64_t mm = (rounds - 1) * kCUs / tiles_n;  // tile rows of the full rounds
+  if (mm < 1 || mm >= tiles_m) return 0;
+  const int64_t tail_tiles = (tiles_m - mm) * tiles_n;
+  const int64_t nk = cdiv(K, 64);
+  int64_t s_max = kCUs / tail_tiles;
+  if (s_max > 16) s_max = 16;
+  if (s_max > nk / 4) s_max = nk / 4;
+  const double tail_rows = (double)(M - mm * T);
+  const double t_plain = (double)rounds * (double)nk * kStepSeconds;
+  const double t_main = (double)cdiv(mm * tiles_n, kCUs) * (double)nk * kStepSeconds + kLaunchSeconds;
+  int64_t best_s = 0;
+  double best_t = 0.95 * t_plain;  // must beat one more round by 5%
+  for (int64_t S = 2; S <= s_max; ++S) {  // more slices: less time per slice, more partial tiles
+    const double ws_bytes = 2.0 * 4.0 * (double)S * tail_rows * (double)N + (double)out_bytes(dtype) * tail_rows * N;
+    const double t = t_main + (double)cdiv(nk, S) * kStepSeconds + ws_bytes / kWorkspaceBytesPerSecond;
+    if (t < best_t) {
+      best_t = t;
+      best_s = S;
+    }
+  }
+  if (best_s < 2) return 0;
+  *m0 = mm * T;
+  return (int)best_s;
+}
+
 // The plan of a tuned choice (vector_loads kept from the automatic plan: it does
 // not depend on the tile for the tiles the tuner tries).
 void apply_choice(const tune_choice& c, int64_t M, int64_t N, int64_t K, gemm_plan_t* p) {
@@ -172,6 +216,8 @@ void apply_choice(const tune_choice& c, int64_t M, int64_t N, int64_t K, gemm_pl
     p->lds_bytes = s.lds;
   }
   p->grid = cdiv(M, c.tm) * cdiv(N, c.tn);
+  p->tail_split_k = 0;
+  p->tail_m0 = 0;
   (void)K;
 }
 
@@ -270,6 +316,15 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
       if (deep >= 0) {
         p.stages = 4;
         p.lds_bytes = tg::kMacroShapes[deep].lds;
+      }
+    }
+    // The last partial round of 256x256 tiles as a split-K tail (automatic plans only).
+    if (p.kernel == 4 && !forced && fs == 0 && p.split_k == 1 && p.tile_m == 256 && p.tile_n == 256) {
+      int64_t m0 = 0;
+      const int ts = tail_split(M, N, K, dtype, &m0);
+      if (ts >= 2) {
+        p.tail_split_k = ts;
+        p.tail_m0 = (int32_t)m0;
       }
     }
     // A plan chosen by gemm_tune for this shape replaces the automatic choice (a
@@ -400,6 +455,66 @@ gemm_status_t gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const 
 
 namespace {
 
+// Enqueue the MFMA kernels of plan p for an M x N part of C (rows of A and C already
+// offset by the caller) with the given K-slice count: one launch, or the slices'
+// partial tiles into the handle's workspace and the ordered reduction.
+gemm_status_t launch_mfma_part(tgemm_handle* h, const gemm_plan_t& p, int splits, bool ta, bool tb, int64_t M,
+                               int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                               int64_t ldc, int dtype, hipStream_t s) {
+  if (splits > 1) {
+    const size_t need = (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+    if (h->ws_bytes < need) {
+      if (h->ws != nullptr) {
+        if (hipFree(h->ws) != hipSuccess) return GEMM_ERR_HIP;
+        h->ws = nullptr;
+        h->ws_bytes = 0;
+      }
+      if (hipMalloc(&h->ws, need) != hipSuccess) {
+        (void)hipGetLastError();
+        h->ws = nullptr;
+        return GEMM_ERR_OUT_OF_MEMORY;
+      }
+      h->ws_bytes = need;
+    }
+  }
+  const int64_t grid = cdiv(M, p.tile_m) * cdiv(N, p.tile_n);
+  tg::MacroArgs a;
+  a.A = (const uint16_t*)A;
+  a.B = (const uint16_t*)B;
+  a.C = C;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.tiles_m = (int)cdiv(M, p.tile_m);
+  a.tiles_n = (int)cdiv(N, p.tile_n);
+  a.group_m = a.tiles_m < 4 ? a.tiles_m : 4;
+  const int64_t nk = cdiv(K, p.tile_k);
+  a.kt_per_split = (int)cdiv(nk, splits);
+  a.split_stride = (int64_t)M * N;
+  a.c_vec = ((uintptr_t)C % (uintptr_t)out_bytes(dtype)) == 0;  // element-aligned C (16-byte stores need no more)
+  hipError_t e;
+  if (p.kernel == 3) {
+    e = tg::launch_small(a, in_kind(dtype), out_kind(dtype), p.vector_loads != 0, s, grid, ta, tb);
+  } else if (splits == 1) {
+    e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k, p.stages), a, in_kind(dtype), out_kind(dtype),
+                         p.vector_loads != 0, s, grid, 1, ta, tb);
+  } else {
+    // partial tiles (fp32, dense, ldc = N) into the workspace, then the ordered reduction
+    tg::MacroArgs w = a;
+    w.C = h->ws;
+    w.ldc = N;
+    w.c_vec = 1;  // hipMalloc'ed workspace: 256-byte aligned fp32
+    e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k, p.stages), w, in_kind(dtype), 0, p.vector_loads != 0,
+                         s, grid, splits, ta, tb);
+    if (e == hipSuccess)
+      e = tg::launch_splitk_reduce((const float*)h->ws, splits, C, ldc, (int)M, (int)N, out_kind(dtype), s);
+  }
+  return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
 // Enqueue the kernels of plan p (arguments already checked).
 gemm_status_t launch_plan(tgemm_handle* h, const gemm_plan_t& p, bool ta, bool tb, int64_t M, int64_t N, int64_t K,
                           const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int dtype,
@@ -429,57 +544,16 @@ gemm_status_t launch_plan(tgemm_handle* h, const gemm_plan_t& p, bool ta, bool t
       break;
     }
     default: {
-      const int splits = p.split_k > 1 ? p.split_k : 1;
-      if (splits > 1) {
-        const size_t need = (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
-        if (h->ws_bytes < need) {
-          if (h->ws != nullptr) {
-            if (hipFree(h->ws) != hipSuccess) return GEMM_ERR_HIP;
-            h->ws = nullptr;
-            h->ws_bytes = 0;
-          }
-          if (hipMalloc(&h->ws, need) != hipSuccess) {
-            (void)hipGetLastError();
-            h->ws = nullptr;
-            return GEMM_ERR_OUT_OF_MEMORY;
-          }
-          h->ws_bytes = need;
-        }
+      if (p.kernel == 4 && p.tail_split_k > 1 && p.tail_m0 > 0 && p.tail_m0 < M) {
+        // the full rounds of tiles, then the tail rows with their K ranges split
+        const int64_t m0 = p.tail_m0;
+        gemm_status_t st = launch_mfma_part(h, p, 1, ta, tb, m0, N, K, A, lda, B, ldb, C, ldc, dtype, s);
+        if (st != GEMM_OK) return st;
+        const void* A2 = (const char*)A + (ta ? m0 : m0 * lda) * 2;
+        void* C2 = (char*)C + m0 * ldc * out_bytes(dtype);
+        return launch_mfma_part(h, p, p.tail_split_k, ta, tb, M - m0, N, K, A2, lda, B, ldb, C2, ldc, dtype, s);
       }
-      tg::MacroArgs a;
-      a.A = (const uint16_t*)A;
-      a.B = (const uint16_t*)B;
-      a.C = C;
-      a.M = (int)M;
-      a.N = (int)N;
-      a.K = (int)K;
-      a.lda = lda;
-      a.ldb = ldb;
-      a.ldc = ldc;
-      a.tiles_m = (int)cdiv(M, p.tile_m);
-      a.tiles_n = (int)cdiv(N, p.tile_n);
-      a.group_m = a.tiles_m < 4 ? a.tiles_m : 4;
-      const int64_t nk = cdiv(K, p.tile_k);
-      a.kt_per_split = (int)cdiv(nk, splits);
-      a.split_stride = (int64_t)M * N;
-      a.c_vec = ((uintptr_t)C % (uintptr_t)out_bytes(dtype)) == 0;  // element-aligned C (16-byte stores need no more)
-      if (p.kernel == 3) {
-        e = tg::launch_small(a, in_kind(dtype), out_kind(dtype), p.vector_loads != 0, s, p.grid, ta, tb);
-      } else if (splits == 1) {
-        e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k, p.stages), a, in_kind(dtype), out_kind(dtype),
-                             p.vector_loads != 0, s, p.grid, 1, ta, tb);
-      } else {
-        // partial tiles (fp32, dense, ldc = N) into the workspace, then the ordered reduction
-        tg::MacroArgs w = a;
-        w.C = h->ws;
-        w.ldc = N;
-        w.c_vec = N % 4 == 0;  // hipMalloc'ed workspace: 256-byte aligned, dense fp32 slices of M x N
-        e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k, p.stages), w, in_kind(dtype), 0, p.vector_loads != 0, s,
-                             p.grid, splits, ta, tb);
-        if (e == hipSuccess)
-          e = tg::launch_splitk_reduce((const float*)h->ws, splits, C, ldc, (int)M, (int)N, out_kind(dtype), s);
-      }
-      break;
+      return launch_mfma_part(h, p, p.split_k > 1 ? p.split_k : 1, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, dtype, s);
     }
   }
   return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
@@ -620,14 +694,28 @@ gemm_status_t gemm_model(const gemm_plan_t* plan, int64_t M, int64_t N, int64_t 
     } else {
       // per K-slice: its K-tiles, plus the zero K-tiles prepended to make their number
       // a multiple of the stage count
-      const int64_t per = cdiv(nk, p.split_k);
       const int64_t ns = p.stages > 0 ? p.stages : 2;
-      double steps = 0;
-      for (int64_t lo = 0; lo < nk; lo += per) {
-        const int64_t n = (nk - lo) < per ? (nk - lo) : per;
-        steps += (double)(n + (ns - n % ns) % ns);
+      auto slice_steps = [&](int64_t splits) {
+        const int64_t per = cdiv(nk, splits);
+        double steps = 0;
+        for (int64_t lo = 0; lo < nk; lo += per) {
+          const int64_t n = (nk - lo) < per ? (nk - lo) : per;
+          steps += (double)(n + (ns - n % ns) % ns);
+        }
+        return steps;
+      };
+      const bool tail = p.tail_split_k > 1 && p.tail_m0 > 0 && p.tail_m0 < M;
+      if (tail) {
+        // the tiles of rows [0, tail_m0) over the whole K range, the tail's tiles in slices
+        const double tiles_main = (double)(cdiv(p.tail_m0, p.tile_m) * tn);
+        const double tiles_tail = (double)m.tiles - tiles_main;
+        const double tile_elems = (double)p.tile_m * p.tile_n;
+        m.executed_flops =
+            2.0 * tile_elems * p.tile_k * (tiles_main * slice_steps(1) + tiles_tail * slice_steps(p.tail_split_k));
+        m.bytes_workspace = 2.0 * 4.0 * (double)p.tail_split_k * (double)(M - p.tail_m0) * dN;
+      } else {
+        m.executed_flops = 2.0 * tile_mn * slice_steps(p.split_k) * p.tile_k;
       }
-      m.executed_flops = 2.0 * tile_mn * steps * p.tile_k;
     }
     if (p.split_k > 1) m.bytes_workspace = 2.0 * 4.0 * (double)p.split_k * dM * dN;
   }

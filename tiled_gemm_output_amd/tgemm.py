@@ -36,7 +36,8 @@ class GemmPlan(ctypes.Structure):
     _fields_ = [("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("vector_loads", ctypes.c_int32), ("kernel", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int32), ("split_k", ctypes.c_int32),
-                ("stages", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("stages", ctypes.c_int32), ("tail_split_k", ctypes.c_int32), ("tail_m0", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         d = {name: getattr(self, name) for name, _ in self._fields_}
