@@ -331,7 +331,11 @@ def main() -> int:
     props = torch.cuda.get_device_properties(0)
     result["device"] = {"arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count}
     result["sclk"] = None
-    if args.clock_window > 0:
+    # Under rocprofv3 its library is loaded into every process this one starts, and it
+    # would bring up the GPU in the amd-smi child before that child starts its own
+    # interpreter: no clock sampling there.
+    profiled = "ROCPROFILER_LIBRARY_CTOR" in os.environ or "ROCPROF_OUTPUT_PATH" in os.environ
+    if args.clock_window > 0 and not profiled:
         samples, max_mhz = sample_clock_under_load(step, args.clock_window)
         if samples:
             med = float(np.median(samples))
