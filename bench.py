@@ -169,6 +169,8 @@ def main() -> int:
     # ~915 us per launch at first, ~795 us from then on); the default warmup covers that.
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="square8192_bf16")
+    ap.add_argument("--shape", default=None,
+                    help="M,N,K replacing the workload's dimensions (same formats, value law and seeds)")
     ap.add_argument("--tile", default=None, help="force a tile, e.g. 256,256,64")
     ap.add_argument("--split-k", type=int, default=0, help="force the K-slice count (0: the library's choice)")
     ap.add_argument("--op", default="nn", choices=["nn", "nt", "tn", "tt"],
@@ -216,6 +218,11 @@ def main() -> int:
         print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
         return 0
     w = inputs.WORKLOADS[args.workload]
+    if args.shape:
+        import dataclasses
+
+        M, N, K = (int(x) for x in args.shape.split(","))
+        w = dataclasses.replace(w, name="%s_as_%dx%dx%d" % (w.name, M, N, K), M=M, N=N, K=K)
     dtype = tgemm.DTYPES[w.dtype]
     log("bench: workload %s M=%d N=%d K=%d dtype=%s" % (w.name, w.M, w.N, w.K, w.dtype))
     a, b = inputs.make(w)

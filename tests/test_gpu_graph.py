@@ -30,10 +30,11 @@ def o():
 
 
 # (M, N, K, dtype, forced tile or None, forced K-slices): the automatic 256x256 plan,
-# a ragged edge-tile plan, split-K with its reduction kernel, the one-wave 16x16x32
-# tile and the int32 path.
+# a ragged edge-tile plan, split-K with its reduction kernel, a split-K tail after the
+# full rounds (three kernels), the one-wave 16x16x32 tile and the int32 path.
 CASES = [
     (512, 512, 1024, tgemm.BF16_BF16, None, 0),
+    (4352, 4096, 1024, tgemm.BF16_BF16, None, 0),
     (1000, 777, 333, tgemm.BF16_F32, (64, 64, 64), 0),
     (128, 2048, 4096, tgemm.BF16_F32, None, 4),
     (128, 128, 128, tgemm.F16_F32, (16, 16, 32), 0),
