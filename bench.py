@@ -191,8 +191,9 @@ def main() -> int:
                          "FETCH_SIZE / WRITE_SIZE readings scale the GEMM's counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
-        log("bench.py: this build runs on one GPU only; --gpus %d is not supported. "
-            "The multi-GPU sharding of this product is described in DESIGN.md." % args.gpus)
+        log("bench.py: one GPU only; --gpus %d is not supported. Across GPUs the product would be split "
+            "by row blocks of C (each GPU holding B), which needs no communication during the product; the "
+            "benchmark measures one GPU's share." % args.gpus)
         return 2
 
     import numpy as np
