@@ -94,7 +94,9 @@ typedef struct {
                                      tiles summed in slice order), so that they fill the compute units
                                      left idle by a last, partial round of tiles */
   int32_t tail_m0;                /* first C row of that tail (a multiple of tile_m; 0 without a tail) */
-  int32_t reserved;               /* 0 */
+  int32_t repack;                 /* bit 0: A, bit 1: B is first copied into rows starting on 128-byte
+                                     boundaries of the handle's workspace (an operand whose rows do
+                                     not; see gemm_set_repack); 0 otherwise */
 } gemm_plan_t;
 
 /* Counts of one planned call (see gemm_model). Counts are held as doubles (exact
@@ -111,7 +113,8 @@ typedef struct {
   double bytes_a;          /* bytes of A the load schedule requests: M K ceil(N / tile_n) elements */
   double bytes_b;          /* bytes of B requested: K N ceil(M / tile_m) elements */
   double bytes_c;          /* bytes of C written: M N elements */
-  double bytes_workspace;  /* split-K partial tiles written and read back (0 without split-K) */
+  double bytes_workspace;  /* split-K partial tiles written and read back, plus operands copied into
+                              aligned rows (read and written once each); 0 without either */
   double compulsory_bytes; /* A and B read once, C written once */
   int64_t tiles;           /* C tiles */
   int64_t k_steps;         /* K-steps per tile over the whole K range: ceil(K / tile_k) */
@@ -189,7 +192,7 @@ gemm_status_t gemm_tune(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t
                         const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                         gemm_dtype_t dtype, void* stream, int32_t iters, gemm_plan_t* best);
 
-/* Release a handle and its split-K workspace (hipFree waits for work still using it).
+/* Release a handle and its workspaces (hipFree waits for work still using them).
  * NULL or an already destroyed handle -> GEMM_ERR_INVALID_ARG. */
 gemm_status_t gemm_destroy(gemm_handle_t h);
 
@@ -212,6 +215,18 @@ gemm_status_t gemm_set_tile(gemm_handle_t h, int32_t tm, int32_t tn, int32_t tk)
  * S * M * N * 4 bytes (see gemm_run). Out of range or a bad handle ->
  * GEMM_ERR_INVALID_ARG. */
 gemm_status_t gemm_set_split_k(gemm_handle_t h, int32_t splits);
+
+/* Operand copies into aligned rows, for later calls on this handle that use the
+ * macro-tile MFMA kernel with 16-byte loads (gemm_plan_t.kernel == 4,
+ * vector_loads == 1). An operand whose rows do not start on 128-byte boundaries
+ * (base, or a leading dimension not a multiple of 64 elements) makes every 128-byte
+ * row segment of a K-tile span two cache lines; copying it first (rows padded to a
+ * multiple of 64 elements, in the handle's workspace) costs one read and one write. mode 0: the library's
+ * choice (copy when the estimated time saved exceeds the copy's, and the copy is at
+ * most 1 GiB); 1: copy every such operand; -1: never copy. The results do not
+ * depend on the mode: the same kernels see the same values in the same order.
+ * Other values or a bad handle -> GEMM_ERR_INVALID_ARG. */
+gemm_status_t gemm_set_repack(gemm_handle_t h, int32_t mode);
 
 /* Validate gemm_run's arguments without a handle and without any HIP call.
  * Returns exactly the status gemm_run would return for an argument error, or

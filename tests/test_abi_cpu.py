@@ -224,6 +224,26 @@ def test_plan_tail_split():
         assert (p["tail_split_k"], p["tail_m0"]) == (0, 0), shape
 
 
+def test_plan_repack():
+    """Automatic operand copies: an operand whose rows do not start on 128-byte
+    boundaries is copied into aligned rows when the estimated time saved (13% of the
+    product's for a K-contiguous operand, 5% for an M/N-contiguous one) exceeds the
+    copy's (one read and one write at 6 TB/s)."""
+    assert plan(8192, 8192, 8192, tgemm.BF16_BF16)["repack"] == 0           # aligned rows
+    assert plan(6000, 6000, 6000, tgemm.BF16_BF16)["repack"] == 1           # 12000-byte rows: A only pays
+    assert plan(10000, 10000, 10000, tgemm.BF16_BF16)["repack"] == 3        # both pay at this size
+    assert plan(8191, 8191, 8191, tgemm.BF16_BF16)["repack"] == 1
+    assert plan(4095, 4095, 4096, tgemm.BF16_BF16)["repack"] == 0           # B only, and it does not pay
+    assert plan(8192, 8192, 8192, tgemm.BF16_BF16, A=0x10040)["repack"] == 1  # base 64 bytes off a line
+    assert plan(8192, 8192, 8192, tgemm.BF16_BF16, lda=8200)["repack"] == 1
+    assert plan(1000, 777, 333, tgemm.BF16_F32)["repack"] == 0              # too small to pay
+    assert plan(8191, 8191, 8191, tgemm.BF16_BF16, A=0x10001)["repack"] == 0  # element loader: no copies
+    p = plan(6000, 6000, 6000, tgemm.BF16_BF16)
+    m = tgemm.gemm_model(p, 6000, 6000, 6000, tgemm.BF16_BF16)
+    tail_ws = 8.0 * p["tail_split_k"] * (6000 - p["tail_m0"]) * 6000
+    assert m["bytes_workspace"] == tail_ws + 2 * 2 * 6000 * 6000  # A read and written once
+
+
 def test_plan_vector_loads_need_alignment():
     """The macro-tile kernel's direct loads need 2-byte aligned A and B only (whole
     16-byte chunks at 2-byte alignment; chunks past a row end are dealt with in the

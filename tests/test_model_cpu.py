@@ -136,5 +136,6 @@ def test_model_of_a_tail_split():
         tail_tiles = (-(-M // tm)) * tiles_n - main_tiles
         want = 2 * tm * tn * tk * (main_tiles * padded_steps(1) + tail_tiles * padded_steps(S))
         assert m["executed_flops"] == want
-        assert m["bytes_workspace"] == 8 * S * (M - p["tail_m0"]) * N
+        copies = (4 * M * K if p["repack"] & 1 else 0) + (4 * K * N if p["repack"] & 2 else 0)  # read + write
+        assert m["bytes_workspace"] == 8 * S * (M - p["tail_m0"]) * N + copies
         assert m["flops"] == 2 * M * N * K

@@ -41,8 +41,11 @@ struct tgemm_handle {
   int cus;
   int tm, tn, tk;   // forced tile, 0 = automatic
   int splits;       // forced K-slice count, 0 = automatic
+  int repack;       // operand copies: 0 automatic, 1 always (rows not 16-byte aligned), -1 never
   void* ws;         // split-K workspace (device memory owned by the handle), or null
   size_t ws_bytes;  // its size
+  void* pack;       // workspace of operand copies (device memory owned by the handle), or null
+  size_t pack_bytes;
   std::unordered_map<tune_key, tune_choice, tune_key_hash> tuned;  // gemm_tune results
 };
 
@@ -76,6 +79,18 @@ constexpr double kStepSeconds = 1.55e-6;
 constexpr double kWorkspaceBytesPerSecond = 4.0e12;
 constexpr double kLaunchSeconds = 3.0e-6;
 constexpr int64_t kMaxRecords = 0x7FFFFFF0LL;  // must match device_common.h
+// Operand copies (automatic choice): the estimated share of the product's time that
+// rows off 128-byte boundaries cost (MI355X, bf16, measured on 8191^3, 8192x8192x8191,
+// 6000^3, 6000x6000x6001 and 4095x4095x4096): ~13% for a K-contiguous operand (its
+// 128-byte row segments span two lines), ~5% for an M/N-contiguous one; the product's
+// rate, the copy's rate (one read and one write), and the largest copy made without
+// being asked.
+constexpr double kMisalignedShareK = 0.13;
+constexpr double kMisalignedShareMN = 0.05;
+constexpr double kProductFlopsPerSecond = 1.3e15;
+constexpr double kCopyBytesPerSecond = 6.0e12;
+constexpr int64_t kMaxAutoRepackBytes = (int64_t)1 << 30;
+constexpr int64_t kRepackAlign = 64;  // elements: rows of copies start on 128-byte boundaries
 
 int out_bytes(int dtype) { return (dtype == GEMM_I32_I32 || dtype == GEMM_F16_F32 || dtype == GEMM_BF16_F32) ? 4 : 2; }
 int in_kind(int dtype) { return (dtype == GEMM_BF16_F32 || dtype == GEMM_BF16_BF16) ? 1 : 0; }  // 1 = bf16
@@ -198,6 +213,48 @@ int tail_split(int64_t M, int64_t N, int64_t K, int dtype, int64_t* m0) {
   return (int)best_s;
 }
 
+// Geometry of a stored 16-bit operand: rows x cols with row stride ld.
+struct Stored {
+  int64_t rows, cols, ld;
+  const void* base;
+  bool kmaj;  // rows run along K (A as given, B supplied transposed)
+};
+int64_t packed_ld(int64_t cols) { return cdiv(cols, kRepackAlign) * kRepackAlign; }
+int64_t packed_bytes(const Stored& x) { return x.rows * packed_ld(x.cols) * 2; }
+// Rows that do not start on 128-byte (cache line) boundaries: every 128-byte K-segment
+// of a K-contiguous row then spans two lines (a 512-byte segment of an M/N-contiguous
+// row five instead of four).
+bool rows_misaligned(const Stored& x) { return ((uintptr_t)x.base & 127) != 0 || ((x.ld * 2) & 127) != 0; }
+
+// Which operands to copy into aligned rows (bit 0 A, bit 1 B): mode 1 every operand
+// whose rows are off 128-byte boundaries; mode 0 those where the estimated time saved
+// (the operand's share of the product's time) exceeds the copy's time and the copy is
+// at most kMaxAutoRepackBytes; -1 none. The copy must keep every tile offset inside a
+// buffer range (as the operand itself does).
+int choose_repack(int mode, int64_t M, int64_t N, int64_t K, const Stored& a, const Stored& b, int bm, int bn,
+                  int bk, bool ta, bool tb) {
+  if (mode < 0) return 0;
+  const double t_product = 2.0 * (double)M * N * K / kProductFlopsPerSecond;
+  int bits = 0;
+  const Stored* ops[2] = {&a, &b};
+  for (int i = 0; i < 2; ++i) {
+    const Stored& x = *ops[i];
+    if (!rows_misaligned(x) || x.rows == 0 || x.cols == 0) continue;
+    if (mode == 0) {
+      const double saved = (x.kmaj ? kMisalignedShareK : kMisalignedShareMN) * t_product;
+      const double cost = 2.0 * 2.0 * (double)x.rows * x.cols / kCopyBytesPerSecond + kLaunchSeconds;
+      if (saved <= cost || packed_bytes(x) > kMaxAutoRepackBytes) continue;
+    }
+    bits |= 1 << i;
+  }
+  // the copies' tile offsets must stay inside a buffer range
+  const uintptr_t aligned = 256;
+  const int64_t lda = (bits & 1) ? packed_ld(a.cols) : a.ld, ldb = (bits & 2) ? packed_ld(b.cols) : b.ld;
+  if (bits && !vector_ok(M, N, K, (const void*)aligned, lda, (const void*)aligned, ldb, bm, bn, bk, ta, tb, true))
+    return 0;
+  return bits;
+}
+
 // The plan of a tuned choice (vector_loads kept from the automatic plan: it does
 // not depend on the tile for the tiles the tuner tries).
 void apply_choice(const tune_choice& c, int64_t M, int64_t N, int64_t K, gemm_plan_t* p) {
@@ -272,6 +329,11 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
                                op_b == GEMM_OP_T, /*relaxed=*/p.kernel == 4)
                          ? 1
                          : 0;
+    if (p.kernel == 4 && p.vector_loads && M > 0 && N > 0 && K > 0) {
+      const bool ta = op_a == GEMM_OP_T, tb = op_b == GEMM_OP_T;
+      const Stored sa{ta ? K : M, ta ? M : K, lda, A, !ta}, sb{tb ? N : K, tb ? K : N, ldb, B, tb};
+      p.repack = choose_repack(h ? h->repack : 0, M, N, K, sa, sb, p.tile_m, p.tile_n, p.tile_k, ta, tb);
+    }
   }
   p.split_k = 1;
   p.stages = p.kernel == 2 ? 1 : 2;
@@ -399,8 +461,11 @@ gemm_status_t gemm_create(gemm_handle_t* out) {
   h->cus = prop.multiProcessorCount;
   h->tm = h->tn = h->tk = 0;
   h->splits = 0;
+  h->repack = 0;
   h->ws = nullptr;
   h->ws_bytes = 0;
+  h->pack = nullptr;
+  h->pack_bytes = 0;
   {
     std::lock_guard<std::mutex> g(g_mu);
     live().insert(h);
@@ -416,6 +481,7 @@ gemm_status_t gemm_destroy(gemm_handle_t h) {
   }
   gemm_status_t st = GEMM_OK;
   if (h->ws != nullptr && hipFree(h->ws) != hipSuccess) st = GEMM_ERR_HIP;  // waits for work using it
+  if (h->pack != nullptr && hipFree(h->pack) != hipSuccess) st = GEMM_ERR_HIP;
   delete h;
   return st;
 }
@@ -434,6 +500,13 @@ gemm_status_t gemm_set_split_k(gemm_handle_t h, int32_t splits) {
   if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
   if (splits < 0 || splits > kMaxSplits) return GEMM_ERR_INVALID_ARG;
   h->splits = splits;
+  return GEMM_OK;
+}
+
+gemm_status_t gemm_set_repack(gemm_handle_t h, int32_t mode) {
+  if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
+  if (mode < -1 || mode > 1) return GEMM_ERR_INVALID_ARG;
+  h->repack = mode;
   return GEMM_OK;
 }
 
@@ -544,6 +617,43 @@ gemm_status_t launch_plan(tgemm_handle* h, const gemm_plan_t& p, bool ta, bool t
       break;
     }
     default: {
+      if (p.kernel == 4 && p.repack != 0) {
+        // copy the flagged operands into aligned rows of the handle's workspace first
+        const Stored sa{ta ? K : M, ta ? M : K, lda, A, !ta}, sb{tb ? N : K, tb ? K : N, ldb, B, tb};
+        const size_t bytes_a = (p.repack & 1) ? (size_t)packed_bytes(sa) : 0;
+        const size_t bytes_b = (p.repack & 2) ? (size_t)packed_bytes(sb) : 0;
+        const size_t off_b = (bytes_a + 255) / 256 * 256, need = off_b + bytes_b;
+        if (h->pack_bytes < need) {
+          if (h->pack != nullptr) {
+            if (hipFree(h->pack) != hipSuccess) return GEMM_ERR_HIP;
+            h->pack = nullptr;
+            h->pack_bytes = 0;
+          }
+          if (hipMalloc(&h->pack, need) != hipSuccess) {
+            (void)hipGetLastError();
+            h->pack = nullptr;
+            return GEMM_ERR_OUT_OF_MEMORY;
+          }
+          h->pack_bytes = need;
+        }
+        gemm_plan_t q = p;
+        q.repack = 0;
+        if (p.repack & 1) {
+          uint16_t* dst = (uint16_t*)h->pack;
+          if (tg::launch_repack((const uint16_t*)A, lda, dst, packed_ld(sa.cols), sa.rows, sa.cols, s) != hipSuccess)
+            return GEMM_ERR_HIP;
+          A = dst;
+          lda = packed_ld(sa.cols);
+        }
+        if (p.repack & 2) {
+          uint16_t* dst = (uint16_t*)((char*)h->pack + off_b);
+          if (tg::launch_repack((const uint16_t*)B, ldb, dst, packed_ld(sb.cols), sb.rows, sb.cols, s) != hipSuccess)
+            return GEMM_ERR_HIP;
+          B = dst;
+          ldb = packed_ld(sb.cols);
+        }
+        return launch_plan(h, q, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, dtype, s);
+      }
       if (p.kernel == 4 && p.tail_split_k > 1 && p.tail_m0 > 0 && p.tail_m0 < M) {
         // the full rounds of tiles, then the tail rows with their K ranges split
         const int64_t m0 = p.tail_m0;
@@ -718,6 +828,9 @@ gemm_status_t gemm_model(const gemm_plan_t* plan, int64_t M, int64_t N, int64_t 
       }
     }
     if (p.split_k > 1) m.bytes_workspace = 2.0 * 4.0 * (double)p.split_k * dM * dN;
+    // operand copies: each flagged operand read and written once
+    if (p.kernel == 4 && (p.repack & 1)) m.bytes_workspace += 2.0 * s_in * dM * dK;
+    if (p.kernel == 4 && (p.repack & 2)) m.bytes_workspace += 2.0 * s_in * dK * dN;
   }
   *out = m;
   return GEMM_OK;

@@ -61,6 +61,12 @@ struct I32Args {
 };
 hipError_t launch_i32(const I32Args& a, hipStream_t s, int64_t grid, int threads, int lds_bytes);
 
+// Copy a rows x cols matrix of 16-bit elements (row stride ld_src) into dst (16-byte
+// aligned, row stride ld_dst >= cols, a multiple of 8), zeros completing the last
+// 16-byte chunk of each row.
+hipError_t launch_repack(const uint16_t* src, int64_t ld_src, uint16_t* dst, int64_t ld_dst, int64_t rows,
+                         int64_t cols, hipStream_t s);
+
 // C[0:M, 0:N] = 0 for element size 2 or 4 bytes.
 hipError_t launch_zero_fill(void* C, int64_t M, int64_t N, int64_t ldc, int elem_bytes, hipStream_t s);
 

@@ -29,6 +29,7 @@ OUT_BYTES = {I32_I32: 4, F16_F32: 4, BF16_F32: 4, BF16_BF16: 2, F16_F16: 2}
 KERNEL_NAMES = {0: "none", 1: "zero_fill", 2: "int32_valu", 3: "mfma_16x16x32_one_wave", 4: "mfma_macro_tile"}
 
 EXPORTS = ["gemm_create", "gemm_run", "gemm_run_op", "gemm_tune", "gemm_destroy", "gemm_set_tile", "gemm_set_split_k",
+           "gemm_set_repack",
            "gemm_check_args", "gemm_check_args_op", "gemm_plan", "gemm_plan_op", "gemm_model", "gemm_status_string"]
 
 
@@ -37,7 +38,7 @@ class GemmPlan(ctypes.Structure):
                 ("threads", ctypes.c_int32), ("vector_loads", ctypes.c_int32), ("kernel", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("stages", ctypes.c_int32), ("tail_split_k", ctypes.c_int32), ("tail_m0", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("repack", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         d = {name: getattr(self, name) for name, _ in self._fields_}
@@ -88,6 +89,8 @@ def load(path: str = LIBRARY):
     lib.gemm_set_tile.restype = i32
     lib.gemm_set_split_k.argtypes = [vp, i32]
     lib.gemm_set_split_k.restype = i32
+    lib.gemm_set_repack.argtypes = [vp, i32]
+    lib.gemm_set_repack.restype = i32
     lib.gemm_check_args.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32]
     lib.gemm_check_args.restype = i32
     lib.gemm_check_args_op.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32]
@@ -130,6 +133,10 @@ def gemm_set_tile(h, tm: int, tn: int, tk: int) -> int:
 
 def gemm_set_split_k(h, splits: int) -> int:
     return load().gemm_set_split_k(h, splits)
+
+
+def gemm_set_repack(h, mode: int) -> int:
+    return load().gemm_set_repack(h, mode)
 
 
 def gemm_run(h, M, N, K, A, lda, B, ldb, C, ldc, dtype, stream=None) -> int:
