@@ -76,7 +76,6 @@ const MacroShape kMacroShapes[kNumMacroShapes] = {
     {256, 128, 64, Cfg256x128::kThreads, Cfg256x128::kLds, Cfg256x128::NS},
     {128, 128, 64, Cfg128x128::kThreads, Cfg128x128::kLds, Cfg128x128::NS},
     {64, 64, 64, Cfg64x64::kThreads, Cfg64x64::kLds, Cfg64x64::NS},
-    {256, 256, 64, Cfg256x256w4::kThreads, Cfg256x256w4::kLds, Cfg256x256w4::NS},
     {128, 128, 64, Cfg128x128s4::kThreads, Cfg128x128s4::kLds, Cfg128x128s4::NS},
     {64, 64, 64, Cfg64x64s4::kThreads, Cfg64x64s4::kLds, Cfg64x64s4::NS},
 };

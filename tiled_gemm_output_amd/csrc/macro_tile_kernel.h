@@ -34,8 +34,9 @@
 //    (ds_read_b128 for K-contiguous tiles; ds_read_b64_tr_b16, which also performs
 //    the transpose MFMA needs, for M/N-contiguous tiles) hit distinct banks;
 //  * XCD-aware, grouped workgroup -> tile order (schedule_tile);
-//  * the C tile of an interior tile is staged through LDS and stored as 16-byte
-//    chunks along its rows (edge tiles: element stores with bounds checks).
+//  * the C tile is staged through LDS and stored as 16-byte chunks along its rows
+//    (edge tiles drop the chunks outside C and store a chunk that crosses N
+//    element by element).
 #pragma once
 
 #include "device_common.h"
@@ -60,7 +61,6 @@ struct MacroCfg {
 };
 
 using Cfg256x256w8 = MacroCfg<256, 256, 64, 2, 4>;  // 8 waves, 128 x 64 per wave
-using Cfg256x256w4 = MacroCfg<256, 256, 64, 2, 2>;  // 4 waves, 128 x 128 per wave
 using Cfg256x128 = MacroCfg<256, 128, 64, 4, 2>;
 using Cfg128x128 = MacroCfg<128, 128, 64, 2, 2>;
 using Cfg64x64 = MacroCfg<64, 64, 64, 2, 2>;
@@ -549,8 +549,8 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   const int64_t ldc = p.ldc;
   char* const Cout = (char*)p.C + (int64_t)blockIdx.y * p.split_stride * (OUT == OUT_F32 ? 4 : 2);
   constexpr int SO = OUT == OUT_F32 ? 4 : 2;  // bytes per output element
-  if (p.c_vec && row0 + BM <= M && col0 + BN <= N) {
-    // Interior tile: each block row (32 rows of the wave tile) goes through
+  if (p.c_vec) {
+    // Each block row (32 rows of the wave tile) goes through
     // a private LDS slice of the stage memory, written as runs of four elements and
     // read back as 16-byte chunks along the rows, so that every global store writes
     // whole 16-byte chunks of consecutive columns (CH lanes per row of the wave
@@ -604,18 +604,48 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
       constexpr int ROWS = 64 / CH;  // rows per 64-lane read
       const int64_t gr0 = (int64_t)(row0 + wm * Cfg::kWTM + 32 * i);
       const int gc0 = col0 + wn * Cfg::kWTN;
+      auto store_chunks = [&](auto EDGE) __attribute__((always_inline)) {
+        constexpr int PER_CHUNK = 16 / SO;  // elements per 16-byte chunk
 #pragma unroll
-      for (int q = 0; q < 32 / ROWS; ++q) {
-        const int rr = q * ROWS + lane / CH, c = lane % CH;
-        i32x4 v = *(TG_LDS i32x4*)(slice + rr * RB + ((c ^ (rr % CH)) << 4));
-        if (SO == 2 && ((rr >> 3) & 1)) v = i32x4{v.z, v.w, v.x, v.y};
-        __builtin_memcpy(Cout + ((gr0 + rr) * ldc + gc0) * SO + 16 * c, &v, 16);  // any element alignment
-      }
+        for (int q = 0; q < 32 / ROWS; ++q) {
+          const int rr = q * ROWS + lane / CH, c = lane % CH;
+          i32x4 v = *(TG_LDS i32x4*)(slice + rr * RB + ((c ^ (rr % CH)) << 4));
+          if (SO == 2 && ((rr >> 3) & 1)) v = i32x4{v.z, v.w, v.x, v.y};
+          char* dst = Cout + ((gr0 + rr) * ldc + gc0) * SO + 16 * c;
+          if constexpr (!decltype(EDGE)::value) {
+            __builtin_memcpy(dst, &v, 16);  // any element alignment
+          } else {
+            // rows past M and columns past N are dropped; a chunk that crosses N is
+            // stored element by element
+            const int64_t row = gr0 + rr;
+            const int col = gc0 + PER_CHUNK * c;
+            if (row < M && col < N) {
+              if (col + PER_CHUNK <= N) {
+                __builtin_memcpy(dst, &v, 16);
+              } else {
+#pragma unroll
+                for (int k = 0; k < PER_CHUNK; ++k) {
+                  if (col + k < N) {
+                    if constexpr (SO == 2)
+                      *(uint16_t*)(dst + 2 * k) = (uint16_t)((uint32_t)v[k / 2] >> (16 * (k % 2)));
+                    else
+                      *(uint32_t*)(dst + 4 * k) = (uint32_t)v[k];
+                  }
+                }
+              }
+            }
+          }
+        }
+      };
+      if (row0 + BM <= M && col0 + BN <= N)
+        store_chunks(IC<0>{});
+      else
+        store_chunks(IC<1>{});
       asm volatile("" ::: "memory");  // the next block row's writes come after these reads
     }
   } else {
-    // Edge tile (or C not aligned to its element size): element by element, dropping
-    // what lies outside C.
+    // C not aligned to its element size: element by element, dropping what lies
+    // outside C.
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = row0 + wm * Cfg::kWTM + 32 * i + (lane & 31);
@@ -675,9 +705,8 @@ static hipError_t launch_layout(int shape, const MacroArgs& a, int in, int out, 
     case 1: return launch_dtype<Cfg256x128, TA, TB>(a, in, out, vec, s, grid, splits);
     case 2: return launch_dtype<Cfg128x128, TA, TB>(a, in, out, vec, s, grid, splits);
     case 3: return launch_dtype<Cfg64x64, TA, TB>(a, in, out, vec, s, grid, splits);
-    case 4: return launch_dtype<Cfg256x256w4, TA, TB>(a, in, out, vec, s, grid, splits);
-    case 5: return launch_dtype<Cfg128x128s4, TA, TB>(a, in, out, vec, s, grid, splits);
-    case 6: return launch_dtype<Cfg64x64s4, TA, TB>(a, in, out, vec, s, grid, splits);
+    case 4: return launch_dtype<Cfg128x128s4, TA, TB>(a, in, out, vec, s, grid, splits);
+    case 5: return launch_dtype<Cfg64x64s4, TA, TB>(a, in, out, vec, s, grid, splits);
     default: return hipErrorInvalidValue;
   }
 }
