@@ -139,16 +139,19 @@ gemm_status_t gemm_create(gemm_handle_t* out);
  *   dtype      one of gemm_dtype_t; element sizes: 4 (i32), 2 (f16, bf16) for A/B;
  *              4 for *_F32 and I32 outputs, 2 for *_BF16 and *_F16 outputs.
  * Errors: GEMM_ERR_INVALID_ARG, GEMM_ERR_UNSUPPORTED_DTYPE, GEMM_ERR_UNSUPPORTED_TILE
- * (a forced tile this dtype has no kernel for), GEMM_ERR_OUT_OF_MEMORY (split-K workspace),
+ * (a forced tile this dtype has no kernel for), GEMM_ERR_OUT_OF_MEMORY (a workspace),
  * GEMM_ERR_HIP (launch failed).
  * Split-K: with the automatic tile choice, a product whose C tiles cannot fill half
- * of the GPU and whose K is long is computed in K-slices (gemm_plan reports split_k).
- * The fp32 partial tiles go to a device workspace owned by the handle: allocated
- * (hipMalloc) on the first call that needs it, grown when a later call needs more
- * (the old one is freed, which waits for work still using it), freed by
- * gemm_destroy. Calls on one handle that use split-K share that workspace, so they
- * must be ordered (one stream, or synchronized between streams). The partial sums
- * are added in a fixed order, so results are reproducible run to run.
+ * of the GPU and whose K is long is computed in K-slices (gemm_plan reports split_k),
+ * and a last, partly full round of tiles may run as a split-K tail (tail_split_k).
+ * The fp32 partial tiles go to a device workspace owned by the handle; operand
+ * copies into line-aligned rows (gemm_plan reports repack; see gemm_set_repack) go
+ * to a second one. Each is allocated (hipMalloc) on the first call that needs it,
+ * grown when a later call needs more (the old one is freed, which waits for work
+ * still using it), and freed by gemm_destroy. Calls on one handle that use a
+ * workspace share it, so they must be ordered (one stream, or synchronized between
+ * streams). Partial sums are added in a fixed order, so results are reproducible
+ * run to run.
  * Stream capture: a call only enqueues kernels on `stream` (no memset, no
  * synchronization), so it may be captured into a HIP graph, provided the handle's
  * workspace is already large enough: a captured call that would have to allocate or
