@@ -60,11 +60,12 @@ class Dev:
         return e0.elapsed_time(e1) * 1e3 / n
 
 
-KEYS = ("kernel", "tile_m", "tile_n", "tile_k", "split_k", "stages", "grid")
+KEYS = ("kernel", "tile_m", "tile_n", "tile_k", "split_k", "stages", "grid", "tail_split_k", "tail_m0", "repack")
 
 
 @pytest.mark.parametrize("shape,dtype", [((200, 136, 1000), tgemm.BF16_F32), ((520, 264, 2000), tgemm.BF16_BF16),
-                                         ((1000, 777, 333), tgemm.BF16_F32), ((96, 96, 96), tgemm.F16_F16)],
+                                         ((1000, 777, 333), tgemm.BF16_F32), ((96, 96, 96), tgemm.F16_F16),
+                                         ((4352, 4096, 1024), tgemm.BF16_BF16)],  # automatic plan with a tail
                          ids=str)
 def test_tuned_plan_used_and_correct(o, shape, dtype):
     M, N, K = shape

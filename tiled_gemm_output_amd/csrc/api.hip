@@ -34,6 +34,7 @@ struct tune_key_hash {
 // A tuned choice: kernel (3 small tile, 4 macro tile), tile, K-slices, LDS stages.
 struct tune_choice {
   int kernel, tm, tn, tk, split_k, stages;
+  int tail_split_k = 0, tail_m0 = 0;  // a split-K tail after the full rounds (the automatic plan's)
 };
 
 struct tgemm_handle {
@@ -273,8 +274,8 @@ void apply_choice(const tune_choice& c, int64_t M, int64_t N, int64_t K, gemm_pl
     p->lds_bytes = s.lds;
   }
   p->grid = cdiv(M, c.tm) * cdiv(N, c.tn);
-  p->tail_split_k = 0;
-  p->tail_m0 = 0;
+  p->tail_split_k = c.tail_split_k;
+  p->tail_m0 = c.tail_m0;
   (void)K;
 }
 
@@ -710,16 +711,19 @@ gemm_status_t gemm_tune(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t
   const bool ta = op_a == GEMM_OP_T, tb = op_b == GEMM_OP_T;
   const bool vec = base.vector_loads != 0;
 
-  // Candidates: every 2-stage macro tile of the 8- and 4-wave kinds with K-slice
-  // counts up to 32 (each slice at least 2 K-tiles), the 4-stage twins where they
-  // apply, and the one-wave 16x16x32 tile for small outputs.
+  // Candidates: the automatic plan when it has a split-K tail, every 2-stage macro
+  // tile with K-slice counts up to 32 (each slice at least 2 K-tiles), the 4-stage
+  // twins where they apply, and the one-wave 16x16x32 tile for small outputs.
   std::vector<tune_choice> cand;
   auto add = [&](const tune_choice& c) {
     for (const tune_choice& d : cand)
-      if (d.kernel == c.kernel && d.tm == c.tm && d.tn == c.tn && d.split_k == c.split_k && d.stages == c.stages)
+      if (d.kernel == c.kernel && d.tm == c.tm && d.tn == c.tn && d.split_k == c.split_k && d.stages == c.stages &&
+          d.tail_split_k == c.tail_split_k && d.tail_m0 == c.tail_m0)
         return;
     cand.push_back(c);
   };
+  if (base.kernel == 4 && base.tail_split_k > 1)
+    add(tune_choice{4, base.tile_m, base.tile_n, base.tile_k, 1, base.stages, base.tail_split_k, base.tail_m0});
   const int shapes[] = {0, 1, 2, 3};
   const int split_try[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
   for (int si : shapes) {
