@@ -612,8 +612,12 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
           i32x4 v = *(TG_LDS i32x4*)(slice + rr * RB + ((c ^ (rr % CH)) << 4));
           if (SO == 2 && ((rr >> 3) & 1)) v = i32x4{v.z, v.w, v.x, v.y};
           char* dst = Cout + ((gr0 + rr) * ldc + gc0) * SO + 16 * c;
+          // C is written once and not read back here: non-temporal stores (1-2% on
+          // products of one round of tiles, where all tiles store at once). The type
+          // carries C's element alignment only: the chunk may straddle 16-byte words.
+          typedef i32x4 i32x4_u __attribute__((aligned(2)));
           if constexpr (!decltype(EDGE)::value) {
-            __builtin_memcpy(dst, &v, 16);  // any element alignment
+            __builtin_nontemporal_store(v, (i32x4_u*)dst);
           } else {
             // rows past M and columns past N are dropped; a chunk that crosses N is
             // stored element by element
@@ -621,7 +625,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
             const int col = gc0 + PER_CHUNK * c;
             if (row < M && col < N) {
               if (col + PER_CHUNK <= N) {
-                __builtin_memcpy(dst, &v, 16);
+                __builtin_nontemporal_store(v, (i32x4_u*)dst);
               } else {
 #pragma unroll
                 for (int k = 0; k < PER_CHUNK; ++k) {
