@@ -485,3 +485,33 @@ def test_many_launches_identical(h, o, name, reps):
     got = c0[torch.from_numpy(rows).cuda()].cpu().numpy()
     ref = o.gemm_rows(a, b, rows, w.in_kind, w.out_kind)
     G.compare(got, ref.view(G.np_int(ob)), w.out_kind)
+
+
+# Pointers at odd byte addresses (the ABI accepts any alignment): A and B then go
+# through the element loader, and C (not aligned to its element size) through the
+# element-by-element epilogue; both must give the oracle's result.
+@pytest.mark.parametrize("dtype", [tgemm.BF16_BF16, tgemm.BF16_F32], ids=["bf16_out", "f32_out"])
+@pytest.mark.parametrize("shape", [(300, 200, 150), (257, 129, 64), (1, 1, 1)], ids=str)
+def test_odd_byte_addresses(h, o, shape, dtype):
+    import torch
+
+    M, N, K = shape
+    a, b = inputs.random_case(M, N, K, "bf16", seed=M + N + K)
+    ob = tgemm.OUT_BYTES[dtype]
+    # byte buffers: each matrix starts one byte into its buffer; the rest holds a fill pattern
+    ba = torch.full((2 * M * K + 64,), 0x5A, dtype=torch.uint8, device="cuda")
+    bb = torch.full((2 * K * N + 64,), 0x5A, dtype=torch.uint8, device="cuda")
+    bc = torch.full((ob * M * N + 64,), 0x5A, dtype=torch.uint8, device="cuda")
+    ba[1:1 + 2 * M * K].copy_(torch.from_numpy(np.ascontiguousarray(a).view(np.uint8).reshape(-1)).cuda())
+    bb[1:1 + 2 * K * N].copy_(torch.from_numpy(np.ascontiguousarray(b).view(np.uint8).reshape(-1)).cuda())
+    p = tgemm.gemm_plan(h, M, N, K, ba.data_ptr() + 1, K, bb.data_ptr() + 1, N, bc.data_ptr() + 1, N, dtype)
+    assert p["vector_loads"] == 0, p
+    print("odd byte addresses %s dtype %d" % (shape, dtype), flush=True)
+    tgemm.check(tgemm.gemm_run(h, M, N, K, ba.data_ptr() + 1, K, bb.data_ptr() + 1, N, bc.data_ptr() + 1, N, dtype,
+                               torch.cuda.current_stream().cuda_stream), "gemm_run")
+    torch.cuda.synchronize()
+    host = bc.cpu().numpy()
+    assert host[0] == 0x5A and np.all(host[1 + ob * M * N:] == 0x5A), "wrote outside C"
+    c = host[1:1 + ob * M * N].copy().view(G.np_int(ob)).reshape(M, N)
+    ref = oracle_ref(o, a, b, dtype).view(G.np_int(ob))
+    G.compare(c, ref, G.OUT_KIND[dtype])
