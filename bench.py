@@ -129,6 +129,18 @@ def cpu_threads() -> int:
     return max(1, min(n, 16))
 
 
+def cpu_model() -> str | None:
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(o, a, b, w, target_s: float):
     """Time the oracle on a bounded set of full rows; return (baseline dict, rows, oracle rows)."""
     import numpy as np
@@ -153,6 +165,8 @@ def cpu_baseline(o, a, b, w, target_s: float):
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "host_cpus": os.cpu_count(),
+        "cpu": cpu_model(),
         "kind": "oracle",
         "sample": "%d of the %d output rows (%d x %d x %d x 2 = %.3g flop, binary64 sums) in %.1f s; "
                   "full product extrapolates to %.0f s" % (n, w.M, n, w.N, w.K, flops, dt,
