@@ -104,3 +104,47 @@ def test_tail_split_large_sampled(h, o, shape):
     got_c = dc[:, torch.from_numpy(cols).cuda()].cpu().numpy()
     G.compare(got_r, o.gemm_rows(a, b, rows, "bf16", "bf16").view(np.int16), "bf16")
     G.compare(got_c, o.gemm_cols(a, b, cols, "bf16", "bf16").view(np.int16), "bf16")
+
+
+def tail_cases():
+    """Tile counts of one or two full rounds plus a few tiles (ragged last tiles),
+    random K, leading-dimension padding and operand forms."""
+    rng = np.random.default_rng(4242)
+    out = []
+    for tm, tn in [(17, 16), (18, 16), (9, 32), (20, 13), (33, 8), (25, 21)]:
+        M = 256 * (tm - 1) + int(rng.integers(1, 257))
+        N = 256 * (tn - 1) + int(rng.integers(1, 257))
+        K = int(rng.integers(1000, 3000))
+        pad = int(rng.choice([0, 1, 8, 37]))
+        ops = [(N_, N_), (T_, N_), (N_, T_), (T_, T_)][int(rng.integers(0, 4))]
+        out.append((M, N, K, pad, ops))
+    return out
+
+
+@pytest.mark.parametrize("case", tail_cases(), ids=str)
+def test_tail_and_copies_random(h, o, case):
+    """Random shapes past one round of 256x256 tiles, with padded leading dimensions
+    and transposed forms: whatever tail and operand copies the plan picks, the sampled
+    rows and columns match the oracle and nothing outside C is written."""
+    import torch
+
+    M, N, K, pad, ops = case
+    a, b = inputs.random_case(M, N, K, "bf16", seed=M + N + K)
+    lda = (M if ops[0] == T_ else K) + pad
+    ldb = (K if ops[1] == T_ else N) + pad
+    sa = np.ascontiguousarray(a.T) if ops[0] == T_ else a
+    sb = np.ascontiguousarray(b.T) if ops[1] == T_ else b
+    da = G.DevMatrix(sa, sa.shape[0], sa.shape[1], lda, 0, 2, fill=G.SENTINEL[2])
+    db = G.DevMatrix(sb, sb.shape[0], sb.shape[1], ldb, 0, 2, fill=G.SENTINEL[2])
+    dc = G.DevMatrix(None, M, N, N + pad, 0, 2)
+    p = tgemm.gemm_plan_op(h, ops[0], ops[1], M, N, K, da.ptr, da.ld, db.ptr, db.ld, dc.ptr, dc.ld, tgemm.BF16_BF16)
+    print("tail/copies random %s plan tail %d m0 %d repack %d" % (case, p["tail_split_k"], p["tail_m0"], p["repack"]),
+          flush=True)
+    tgemm.check(tgemm.gemm_run_op(h, ops[0], ops[1], M, N, K, da.ptr, da.ld, db.ptr, db.ld, dc.ptr, dc.ld,
+                                  tgemm.BF16_BF16, torch.cuda.current_stream().cuda_stream), "gemm_run_op")
+    torch.cuda.synchronize()
+    assert dc.untouched_outside()
+    c = dc.host()
+    rows, cols = inputs.sample_rows_cols(M, N, seed=M, block=256)
+    G.compare(c[rows], o.gemm_rows(a, b, rows, "bf16", "bf16").view(np.int16), "bf16")
+    G.compare(c[:, cols], o.gemm_cols(a, b, cols, "bf16", "bf16").view(np.int16), "bf16")
