@@ -15,9 +15,9 @@ accumulation, bf16 output). Prints ONE JSON line on stdout:
   cpu_baseline the oracle (plain CPU triple loop, binary64 sums) timed on a
                bounded sample of rows of the same product on the host cores
   check        the sampled rows of the GPU result against those oracle rows
-  sclk         the gfx clock under the same load (amd-smi, sampled while the
-               launches continue after the timed region) and the MFMA peak and
-               fraction at that clock
+  sclk         the gfx clock and socket power under the same load (amd-smi,
+               sampled while the launches continue after the timed region) and
+               the MFMA peak and fraction at that clock
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 """
@@ -66,12 +66,13 @@ def load_traffic(workload: str, sha: str):
 
 
 def smi_gfx_clock_mhz():
-    """Current gfx clock of GPU 0 from `amd-smi metric -c`, averaged over its XCDs (MHz),
-    and the reported maximum; (None, None) when the tool or its output is not usable."""
+    """Current gfx clock of GPU 0 from `amd-smi metric -p -c`, averaged over its XCDs (MHz),
+    the reported maximum clock and the socket power (W); Nones when the tool or its
+    output is not usable."""
     import subprocess
 
     try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"], capture_output=True, text=True,
                            timeout=15)
         data = json.loads(r.stdout)
         gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
@@ -80,16 +81,23 @@ def smi_gfx_clock_mhz():
         top = [v["max_clk"]["value"] for k, v in clocks.items() if k.startswith("gfx_") and isinstance(v, dict)]
         cur = [float(x) for x in cur if isinstance(x, (int, float))]
         top = [float(x) for x in top if isinstance(x, (int, float))]
+        watts = None
+        try:
+            w = gpu["power"]["socket_power"]["value"]
+            watts = float(w) if isinstance(w, (int, float)) else None
+        except (KeyError, TypeError):
+            pass
         if not cur:
-            return None, None
-        return sum(cur) / len(cur), (max(top) if top else None)
+            return None, None, None
+        return sum(cur) / len(cur), (max(top) if top else None), watts
     except Exception:
-        return None, None
+        return None, None, None
 
 
 def sample_clock_under_load(step, seconds: float):
-    """Keep launching ``step`` for ``seconds`` while sampling the gfx clock with amd-smi
-    in a second thread; returns the samples (MHz) and the reported maximum clock."""
+    """Keep launching ``step`` for ``seconds`` while sampling the gfx clock and socket power
+    with amd-smi in a second thread; returns the clock samples (MHz), the power samples
+    (W), both taken while the launches were running, and the reported maximum clock."""
     import threading
 
     import torch
@@ -99,10 +107,10 @@ def sample_clock_under_load(step, seconds: float):
 
     def sampler():
         while not stop.is_set():
-            mhz, mx = smi_gfx_clock_mhz()
+            mhz, mx, watts = smi_gfx_clock_mhz()
             if mhz is None:
                 return
-            samples.append((time.perf_counter(), mhz))
+            samples.append((time.perf_counter(), mhz, watts))
             top[0] = mx
 
     th = threading.Thread(target=sampler, daemon=True)
@@ -118,7 +126,8 @@ def sample_clock_under_load(step, seconds: float):
     stop.set()
     th.join(timeout=20)
     # only readings completed while the launches were still running
-    return [mhz for t, mhz in samples if t <= load_end], top[0]
+    kept = [(mhz, watts) for t, mhz, watts in samples if t <= load_end]
+    return [m for m, _ in kept], [w for _, w in kept if w is not None], top[0]
 
 
 def cpu_threads() -> int:
@@ -358,18 +367,20 @@ def main() -> int:
     # interpreter: no clock sampling there.
     profiled = "ROCPROFILER_LIBRARY_CTOR" in os.environ or "ROCPROF_OUTPUT_PATH" in os.environ
     if args.clock_window > 0 and not profiled:
-        samples, max_mhz = sample_clock_under_load(step, args.clock_window)
+        samples, watts, max_mhz = sample_clock_under_load(step, args.clock_window)
         if samples:
             med = float(np.median(samples))
             top = max_mhz or 2400.0
             peak_now = PEAK_MFMA_16BIT_TFLOPS * med / top
             result["sclk"] = {
-                "source": "amd-smi metric -c (gfx clock, mean over XCDs), sampled while the same launches "
+                "source": "amd-smi metric -p -c (gfx clock, mean over XCDs; socket power), sampled while the same launches "
                           "continue for %.1f s after the timed region" % args.clock_window,
                 "median_mhz": med, "min_mhz": float(np.min(samples)), "max_mhz": float(np.max(samples)),
                 "samples": len(samples), "max_clk_mhz": top,
                 "mfma_peak_at_median_tflops": peak_now,
                 "frac_of_peak_at_median": (flops / (launch_ms * 1e-3) / 1e12) / peak_now,
+                "socket_power_w_median": float(np.median(watts)) if watts else None,
+                "socket_power_w_max": float(np.max(watts)) if watts else None,
             }
     if not args.no_cpu_baseline:
         import oracle
