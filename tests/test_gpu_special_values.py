@@ -7,7 +7,9 @@ times zero is NaN, and infinities of both signs in one sum give NaN. The oracle 
 binary64 under the same IEEE rules, so the NaN positions and the infinities of C must
 match it exactly; every finite element follows the accuracy rule. Sums beyond the
 output format's largest finite value round to an infinity on both sides (fp16 output:
-65504 + 16 rounds to even, i.e. up to infinity; 65504 + 15 stays 65504).
+65504 + 16 rounds to even, i.e. up to infinity; 65504 + 15 stays 65504). Subnormal
+inputs and fp32 subnormal results keep their values (no flush to zero): with inputs
+whose products and sums are exact in fp32, C equals the oracle bit for bit.
 """
 import numpy as np
 import pytest
@@ -130,3 +132,44 @@ def test_output_overflow(h, o, dtype):
     c, dc = G.run(h, a, b, dtype)
     assert dc.untouched_outside()
     check_special(c, ref, okind)
+
+
+@pytest.mark.parametrize("dtype", FLOAT_DTYPES)
+@pytest.mark.parametrize("tile", [None, (256, 256, 64), (16, 16, 32)], ids=["auto", "t256", "t16"])
+def test_subnormal_inputs_and_outputs(h, o, dtype, tile):
+    """Subnormal inputs count at their value (gradual underflow, no flush to zero): fp16
+    2^-20 and 2^-24 (subnormal in fp16, normal in fp32 once multiplied by 1), bf16 2^-130
+    times 2^100 (normal product); and fp32 results below 2^-126 (bf16 2^-70 x 2^-72,
+    summed) are kept as fp32 subnormals."""
+    kind, okind = G.IN_KIND[dtype], G.OUT_KIND[dtype]
+    M, N, K = 96, 80, 100
+    rng = np.random.default_rng(dtype)
+    x = np.zeros((M, K), np.float32)
+    y = np.zeros((K, N), np.float32)
+    if kind == "f16":
+        x[:, :] = np.float32(2.0 ** -20) * rng.integers(1, 16, size=(M, K)).astype(np.float32)  # subnormal in fp16
+        x[0::3, :] = np.float32(2.0 ** -24)  # the smallest fp16 subnormal
+        y[:, :] = rng.integers(-3, 4, size=(K, N)).astype(np.float32)
+    else:
+        x[:, :] = np.float32(2.0 ** -130) * rng.integers(1, 8, size=(M, K)).astype(np.float32)  # subnormal in bf16
+        y[:, :] = np.float32(2.0 ** 100) * rng.integers(-3, 4, size=(K, N)).astype(np.float32)
+        x[0::4, :] = np.float32(2.0 ** -70) * rng.integers(1, 8, size=(M // 4, K)).astype(np.float32)
+        y[:, 0::5] = np.float32(2.0 ** -72) * rng.integers(-3, 4, size=(K, N // 5)).astype(np.float32)
+    a, b = inputs.to_bits(x, kind), inputs.to_bits(y, kind)
+    # the stored inputs are exactly the intended values
+    assert np.array_equal(G.values(a, kind if kind == "f16" else "bf16"), x.astype(np.float64))
+    ref = o.gemm(a, b, kind, okind).view(G.np_int(tgemm.OUT_BYTES[dtype]))
+    r = G.values(ref, okind)
+    if kind == "bf16" and okind == "f32":
+        sub = (np.abs(r) < 2.0 ** -126) & (r != 0)
+        assert sub.sum() > 0  # some results are fp32 subnormals
+    tgemm.check(tgemm.gemm_set_tile(h, *(tile or (0, 0, 0))), "gemm_set_tile")
+    try:
+        print("subnormals dtype %d tile %s" % (dtype, tile), flush=True)
+        c, dc = G.run(h, a, b, dtype)
+    finally:
+        tgemm.gemm_set_tile(h, 0, 0, 0)
+    assert dc.untouched_outside()
+    # exact: every product and partial sum is exact in fp32 (integer multiples of one power of two)
+    cv = G.values(c, okind)
+    assert np.array_equal(cv, r), "max |C - R| %g at |R| %g" % (np.max(np.abs(cv - r)), np.max(np.abs(r)))
