@@ -129,6 +129,16 @@ def test_large_workloads_sampled(h, o, name):
     sampled_check(h, o, a, b, tgemm.DTYPES[w.dtype], rows, cols)
 
 
+@pytest.mark.parametrize("dtype", [tgemm.F16_F16, tgemm.F16_F32])
+def test_large_f16_sampled(h, o, dtype):
+    """fp16 inputs at the full 8192^3 size (N(0, 1) draws rounded to fp16; the sums, up to
+    a few hundred, stay far inside fp16's range), on sampled rows and columns."""
+    a, b = inputs.random_case(8192, 8192, 8192, "f16", seed=8192 + dtype)
+    rows, cols = inputs.sample_rows_cols(8192, 8192, seed=dtype, block=512)
+    print("large f16 8192^3 dtype %d" % dtype, flush=True)
+    sampled_check(h, o, a, b, dtype, rows, cols)
+
+
 @pytest.mark.parametrize("name", ["square8192_bf16", "skinny128x8192x8192_bf16"])
 def test_large_exact_integer_inputs(h, o, name):
     """Integer-valued inputs in [-8, 8]: every fp32 partial sum is exact, so the

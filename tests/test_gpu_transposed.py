@@ -137,7 +137,8 @@ def test_transposed_split_k(h, o, ops, splits):
         check(h, o, a, b, tgemm.BF16_F32, ops, splits=splits)
 
 
-@pytest.mark.parametrize("name,ops", [("square8192_bf16", (N_, T_)), ("skinny128x8192x8192_bf16", (N_, T_)),
+@pytest.mark.parametrize("name,ops", [("square8192_bf16", (N_, T_)), ("square8192_bf16", (T_, N_)),
+                                      ("square8192_bf16", (T_, T_)), ("skinny128x8192x8192_bf16", (N_, T_)),
                                       ("tall16384x1024x8192_bf16", (T_, N_))], ids=str)
 def test_transposed_large_sampled(h, o, name, ops):
     """Full-size products in the forms real callers use most (weights stored N x K),
