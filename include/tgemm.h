@@ -49,8 +49,18 @@ extern "C" {
 
 typedef struct tgemm_handle* gemm_handle_t;
 
+/* The enumerations below are 32-bit integers in the ABI. Compiled as C++ (the library
+ * itself) they have int32_t as their fixed underlying type, so that every int32 a C
+ * caller may pass (an unknown dtype, say) is a value of the type, which the argument
+ * checks then reject, and never a value outside the enumeration's range. */
+#ifdef __cplusplus
+#define TGEMM_ENUM_BASE : int32_t
+#else
+#define TGEMM_ENUM_BASE
+#endif
+
 /* Status codes (int32). */
-typedef enum {
+typedef enum TGEMM_ENUM_BASE {
   GEMM_OK = 0,
   GEMM_ERR_INVALID_ARG = 1,       /* null/negative/too-small argument, destroyed or null handle */
   GEMM_ERR_UNSUPPORTED_DTYPE = 2, /* dtype is not one of gemm_dtype_t */
@@ -62,7 +72,7 @@ typedef enum {
 } gemm_status_t;
 
 /* Input/accumulator/output formats (int32). */
-typedef enum {
+typedef enum TGEMM_ENUM_BASE {
   GEMM_I32_I32 = 0,   /* int32 in, int32 accumulate (wraps mod 2^32), int32 out */
   GEMM_F16_F32 = 1,   /* IEEE binary16 in, fp32 accumulate, fp32 out */
   GEMM_BF16_F32 = 2,  /* bfloat16 in, fp32 accumulate, fp32 out */
@@ -71,7 +81,7 @@ typedef enum {
 } gemm_dtype_t;
 
 /* Operand forms (int32) for the *_op entry points: op(X) = X or X^T. */
-typedef enum {
+typedef enum TGEMM_ENUM_BASE {
   GEMM_OP_N = 0, /* as given: A stored M x K (lda >= K), B stored K x N (ldb >= N) */
   GEMM_OP_T = 1  /* transposed: A stored K x M (lda >= M), B stored N x K (ldb >= K) */
 } gemm_op_t;

@@ -97,7 +97,45 @@ static int gpu_mode(void) {
   return 0;
 }
 
+/* Every planning path on the host: shapes from empty to past one round of 256x256
+ * tiles, padded and odd leading dimensions, odd and even addresses, all operand forms
+ * and dtypes. Each plan must be accepted, and its counts must hold 2MNK flops. */
+static int sweep_mode(void) {
+  static const int64_t dims[] = {0, 1, 7, 16, 63, 64, 65, 255, 256, 257, 1000, 4095, 4352, 8191, 8193, 20000};
+  static const int64_t pads[] = {0, 1, 8, 64};
+  static const uintptr_t bases[] = {0x100000, 0x100002, 0x100001};
+  const int nd = (int)(sizeof(dims) / sizeof(dims[0]));
+  long plans = 0;
+  for (int dt = 0; dt <= 4; ++dt)
+    for (int op = 0; op < 4; ++op)
+      for (int im = 0; im < nd; ++im)
+        for (int in = 0; in < nd; in += 2)
+          for (int ik = (im + in) % 3; ik < nd; ik += 3) {
+            const int64_t M = dims[im], N = dims[in], K = dims[ik];
+            const gemm_op_t oa = (op & 1) ? GEMM_OP_T : GEMM_OP_N, ob = (op & 2) ? GEMM_OP_T : GEMM_OP_N;
+            const int64_t pad = pads[(im + ik) % 4];
+            const int64_t lda = (oa == GEMM_OP_T ? M : K) + pad, ldb = (ob == GEMM_OP_T ? K : N) + pad, ldc = N + pad;
+            const void* A = (const void*)bases[(im + in) % 3];
+            const void* B = (const void*)bases[(in + ik) % 3];
+            void* C = (void*)bases[(im + 2 * ik) % 3];
+            const gemm_dtype_t dtype = (gemm_dtype_t)dt;
+            const gemm_status_t chk = gemm_check_args_op(oa, ob, M, N, K, A, lda, B, ldb, C, ldc, dtype);
+            gemm_plan_t plan;
+            gemm_model_t model;
+            const gemm_status_t st = gemm_plan_op(NULL, oa, ob, M, N, K, A, lda, B, ldb, C, ldc, dtype, &plan);
+            EXPECT(st == chk);
+            if (st != GEMM_OK) continue;
+            EXPECT(gemm_model(&plan, M, N, K, dtype, &model) == GEMM_OK);
+            EXPECT(model.flops == 2.0 * (double)M * (double)N * (double)K);
+            ++plans;
+          }
+  EXPECT(plans > 5000);
+  printf("abi_client sweep: ok (%ld plans)\n", plans);
+  return 0;
+}
+
 int main(int argc, char** argv) {
   if (argc > 1 && strcmp(argv[1], "gpu") == 0) return gpu_mode();
+  if (argc > 1 && strcmp(argv[1], "sweep") == 0) return sweep_mode();
   return host_mode();
 }
