@@ -525,3 +525,51 @@ def test_odd_byte_addresses(h, o, shape, dtype):
     c = host[1:1 + ob * M * N].copy().view(G.np_int(ob)).reshape(M, N)
     ref = oracle_ref(o, a, b, dtype).view(G.np_int(ob))
     G.compare(c, ref, G.OUT_KIND[dtype])
+
+
+@pytest.mark.parametrize("tile", [(64, 64, 64), (128, 128, 64), (256, 128, 64), (256, 256, 64)], ids=str)
+def test_k_step_counts(h, o, tile):
+    """Stage bookkeeping at the smallest K-step counts: 1 to 6 K-tiles (full, and with a
+    partial last K-tile), 2 x 2 ragged tiles, integer-valued inputs (exact in any order):
+    every run matches the oracle bit for bit and a second run repeats it."""
+    tm, tn, tk = tile
+    M, N = tm + 17, tn + 5
+    for nk in range(1, 7):
+        for K in (tk * nk, tk * nk - 13):
+            a = inputs.draw((M, K), "small_int", "bf16", 100 + K)
+            b = inputs.draw((K, N), "small_int", "bf16", 200 + K)
+            ref = oracle_ref(o, a, b, tgemm.BF16_F32).view(np.int32)
+            set_tile(h, tile)
+            try:
+                print("k-steps tile %s K %d" % (tile, K), flush=True)
+                c1, _ = G.run(h, a, b, tgemm.BF16_F32)
+                c2, _ = G.run(h, a, b, tgemm.BF16_F32)
+            finally:
+                set_tile(h, None)
+            assert np.array_equal(c1, ref), (tile, K)
+            assert np.array_equal(c2, c1), (tile, K)
+
+
+@pytest.mark.parametrize("tile", [(64, 64, 64), (128, 128, 64)], ids=str)
+def test_k_step_counts_four_stages(h, o, tile):
+    """The 4-stage twins (launches of at most 256 workgroups with 8-15 K-tiles in a multiple
+    of 4, or at least 16): K-tile counts around those thresholds, with the zero K-tiles
+    that pad the count to a multiple of 4, exact against the oracle."""
+    tm, tn, tk = tile
+    M, N = 2 * tm + 3, 3 * tn - 7
+    seen = set()
+    for nk in (8, 12, 16, 17, 18, 19):
+        for K in (tk * nk, tk * nk - 5):
+            a = inputs.draw((M, K), "small_int", "f16", 300 + K)
+            b = inputs.draw((K, N), "small_int", "f16", 400 + K)
+            ref = oracle_ref(o, a, b, tgemm.F16_F32).view(np.int32)
+            set_tile(h, tile)
+            try:
+                p = tgemm.gemm_plan(h, M, N, K, 1 << 20, K, 1 << 30, N, 1 << 34, N, tgemm.F16_F32)
+                seen.add(p["stages"])
+                print("4-stage k-steps tile %s K %d stages %d" % (tile, K, p["stages"]), flush=True)
+                c, _ = G.run(h, a, b, tgemm.F16_F32)
+            finally:
+                set_tile(h, None)
+            assert np.array_equal(c, ref), (tile, K, p["stages"])
+    assert 4 in seen, seen
