@@ -29,16 +29,19 @@ def o():
     return oracle.get()
 
 
-# (M, N, K, dtype, forced tile or None, forced K-slices): the automatic 256x256 plan,
-# a ragged edge-tile plan, split-K with its reduction kernel, a split-K tail after the
-# full rounds (three kernels), the one-wave 16x16x32 tile and the int32 path.
+# (M, N, K, dtype, forced tile or None, forced K-slices, operand-copy mode): the automatic
+# 256x256 plan, a ragged edge-tile plan, split-K with its reduction kernel, a split-K tail
+# after the full rounds (three kernels), the one-wave 16x16x32 tile, the int32 path, and
+# plans that first copy A into aligned rows (alone, and before a split-K tail).
 CASES = [
-    (512, 512, 1024, tgemm.BF16_BF16, None, 0),
-    (4352, 4096, 1024, tgemm.BF16_BF16, None, 0),
-    (1000, 777, 333, tgemm.BF16_F32, (64, 64, 64), 0),
-    (128, 2048, 4096, tgemm.BF16_F32, None, 4),
-    (128, 128, 128, tgemm.F16_F32, (16, 16, 32), 0),
-    (96, 80, 70, tgemm.I32_I32, None, 0),
+    (512, 512, 1024, tgemm.BF16_BF16, None, 0, 0),
+    (4352, 4096, 1024, tgemm.BF16_BF16, None, 0, 0),
+    (1000, 777, 333, tgemm.BF16_F32, (64, 64, 64), 0, 0),
+    (128, 2048, 4096, tgemm.BF16_F32, None, 4, 0),
+    (128, 128, 128, tgemm.F16_F32, (16, 16, 32), 0, 0),
+    (96, 80, 70, tgemm.I32_I32, None, 0, 0),
+    (1000, 1024, 1000, tgemm.BF16_BF16, None, 0, 1),
+    (4352, 4096, 1000, tgemm.BF16_F32, None, 0, 1),
 ]
 
 
@@ -48,8 +51,9 @@ def _inputs(M, N, K, dtype, seed):
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "%dx%dx%d-d%d" % c[:4])
 def test_graph_replays_match_eager(o, case):
-    M, N, K, dtype, tile, splits = case
-    print("graph case M=%d N=%d K=%d dtype=%d tile=%s split_k=%d" % (M, N, K, dtype, tile, splits), flush=True)
+    M, N, K, dtype, tile, splits, repack = case
+    print("graph case M=%d N=%d K=%d dtype=%d tile=%s split_k=%d repack=%d" % (M, N, K, dtype, tile, splits, repack),
+          flush=True)
     a, b = _inputs(M, N, K, dtype, 7 + M)
     it = np.int32 if dtype == tgemm.I32_I32 else np.int16
     da, db = torch.from_numpy(a.view(it)).cuda(), torch.from_numpy(b.view(it)).cuda()
@@ -60,6 +64,11 @@ def test_graph_replays_match_eager(o, case):
         if tile:
             tgemm.check(tgemm.gemm_set_tile(h, *tile))
         tgemm.check(tgemm.gemm_set_split_k(h, splits))
+        tgemm.check(tgemm.gemm_set_repack(h, repack))
+        if repack:
+            p = tgemm.gemm_plan(h, M, N, K, da.data_ptr(), K, db.data_ptr(), N, dc.data_ptr(), N, dtype)
+            assert p["repack"] & 1, p  # A (rows of K elements, not a multiple of 64) is copied
+            assert M < 4352 or p["tail_split_k"] > 1, p  # and the larger case ends with a split-K tail
 
         def call(stream):
             tgemm.check(tgemm.gemm_run(h, M, N, K, da.data_ptr(), K, db.data_ptr(), N, dc.data_ptr(), N, dtype, stream))
