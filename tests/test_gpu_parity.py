@@ -573,3 +573,22 @@ def test_k_step_counts_four_stages(h, o, tile):
                 set_tile(h, None)
             assert np.array_equal(c, ref), (tile, K, p["stages"])
     assert 4 in seen, seen
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1 << 20), (100000, 1, 512), (1, 100000, 512), (3, 70000, 3),
+                                   (70000, 3, 5), (2, 2, 300001)], ids=str)
+def test_degenerate_shapes(h, o, shape):
+    """One output with a reduction of 2^20, a single column or row of 100,000 outputs,
+    and thin products with K of 3 to 300,001: the whole C against the oracle, nothing
+    written outside C; with integer-valued inputs, bit for bit."""
+    M, N, K = shape
+    print("degenerate %s" % (shape,), flush=True)
+    a, b = inputs.random_case(M, N, K, "bf16", seed=M + 7 * N + K)
+    c, dc = G.run(h, a, b, tgemm.BF16_F32)
+    assert dc.untouched_outside()
+    G.compare(c, oracle_ref(o, a, b, tgemm.BF16_F32).view(np.int32), "f32")
+    if K <= 300001:
+        ai = inputs.draw((M, K), "small_int", "bf16", 5 + M)
+        bi = inputs.draw((K, N), "small_int", "bf16", 6 + N)
+        c, _ = G.run(h, ai, bi, tgemm.BF16_F32)
+        assert np.array_equal(c, oracle_ref(o, ai, bi, tgemm.BF16_F32).view(np.int32))
