@@ -97,8 +97,11 @@ typedef struct {
   int32_t lds_bytes;              /* LDS per workgroup */
   int32_t split_k;                /* K-slices: 1, or S > 1 when each tile's reduction is cut into S
                                      slices whose fp32 partial tiles a second kernel sums in slice order */
-  int32_t stages;                 /* LDS stages of the K-tile pipeline (macro-tile kernel: 2, or 4 when
-                                     the launch has at most one workgroup per compute unit) */
+  int32_t stages;                 /* B stages of the macro-tile kernel's LDS pipeline: 2 (K-tiles loaded
+                                     two K-steps ahead into three A stages and two B stages), or 4 (loaded
+                                     three K-steps ahead into four stages of each) when the launch has
+                                     at most one workgroup per compute unit; 2 for the 16x16x32 tile (two
+                                     stages of each), 1 for the int32 kernel, 0 when nothing is launched */
   int32_t tail_split_k;           /* 0, or S > 1: the tiles of C rows [tail_m0, M) run after the others
                                      as a second launch of the same tile with S K-slices (fp32 partial
                                      tiles summed in slice order), so that they fill the compute units
@@ -117,9 +120,8 @@ typedef struct {
  * since the kernels load nothing outside the matrices. */
 typedef struct {
   double flops;            /* 2 M N K, the algorithmic operation count */
-  double executed_flops;   /* multiply-adds x 2 the kernel executes, zero padding of partial
-                              tiles and of the K range included (each K-slice of the macro-tile
-                              kernel is padded with zero K-tiles to a multiple of plan.stages) */
+  double executed_flops;   /* multiply-adds x 2 the kernel executes, the zero padding of partial
+                              tiles (to whole tile_m x tile_n x tile_k blocks) included */
   double bytes_a;          /* bytes of A the load schedule requests: M K ceil(N / tile_n) elements */
   double bytes_b;          /* bytes of B requested: K N ceil(M / tile_m) elements */
   double bytes_c;          /* bytes of C written: M N elements */

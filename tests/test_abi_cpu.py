@@ -165,7 +165,7 @@ def test_plan_tile_by_rounds_of_workgroups():
     assert tile(3072, 4096, 1024) == (256, 256, 1, 2)
     assert tile(2560, 2560, 2560)[:2] == (128, 128)     # 100 of 256x256 would leave 156 CUs idle
     assert tile(1024, 1024, 1024) == (64, 64, 1, 4)     # short K: 256 tiles of 64x64, 16 K-tiles each
-    assert tile(512, 512, 512) == (64, 64, 1, 4)        # 8 K-tiles, a multiple of the 4 stages
+    assert tile(512, 512, 512) == (64, 64, 1, 4)        # 8 K-tiles
     assert tile(1536, 1536, 1536)[:2] == (128, 128)     # 144 tiles of 128x128
     assert tile(128, 8192, 8192)[:3] == (128, 128, 4)   # long K: one row of 128x128 tiles reads B once
     assert tile(64, 4096, 4096)[:3] == (64, 64, 4)
@@ -190,15 +190,16 @@ def test_plan_split_k():
 
 
 def test_plan_stages():
-    """4 LDS stages when the launch has at most one workgroup per compute unit (256)
-    and every K-slice has at least 16 K-tiles, or 8 to 15 in a multiple of 4 (no zero
-    padding tile); 2 otherwise."""
+    """The deep pipeline (4 stages of each operand) when the launch has at most one
+    workgroup per compute unit (256) and every K-slice has at least 8 K-tiles; the
+    default one (3 A stages, 2 B stages) otherwise."""
     assert plan(8192, 8192, 8192, tgemm.BF16_BF16)["stages"] == 2             # 1024 workgroups
     p = plan(128, 8192, 8192, tgemm.BF16_F32)                                  # 64 tiles x 4 slices of 32 K-tiles
     assert (p["grid"] * p["split_k"], p["stages"]) == (256, 4)
     p = plan(1792, 1792, 1096, tgemm.BF16_BF16)                                # 196 tiles, 18 K-tiles (ragged K)
     assert (p["tile_m"], p["grid"], p["split_k"], p["stages"]) == (128, 196, 1, 4)
-    assert plan(1792, 1792, 900, tgemm.BF16_BF16)["stages"] == 2              # 15 K-tiles: too short
+    assert plan(1792, 1792, 900, tgemm.BF16_BF16)["stages"] == 4              # 15 K-tiles
+    assert plan(1792, 1792, 448, tgemm.BF16_BF16)["stages"] == 2              # 7 K-tiles: too short
     assert plan(1792, 1794, 1096, tgemm.BF16_BF16)["stages"] == 4             # odd N: still direct loads
     assert plan(1792, 1792, 1096, tgemm.BF16_BF16, A=0x10001)["stages"] == 2  # odd address: element loader
     assert plan(9, 9, 9, tgemm.I32_I32)["stages"] == 1

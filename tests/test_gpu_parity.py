@@ -352,9 +352,9 @@ DEEP = [(1792, 1792, 1096), (1000, 1000, 4096), (136, 2056, 4096), (200, 968, 80
 @pytest.mark.parametrize("shape", DEEP, ids=str)
 def test_deep_pipeline(h, o, shape):
     """Launches of at most one workgroup per compute unit run the 4-stage twin of
-    the tile (zero K-tiles pad each slice to a multiple of 4, ragged K tails, edge
-    tiles, split-K): random inputs to the accuracy rule, integer-valued inputs bit
-    for bit, in every format and in the transposed forms."""
+    the tile (K-tile counts that are not a multiple of the 4-step stage cycle,
+    ragged K tails, edge tiles, split-K): random inputs to the accuracy rule,
+    integer-valued inputs bit for bit, in every format and in the transposed forms."""
     M, N, K = shape
     for n, dtype in enumerate([tgemm.BF16_BF16, tgemm.F16_F32, tgemm.BF16_F32, tgemm.F16_F16]):
         p = plan_of(h, M, N, K, dtype)
@@ -412,14 +412,15 @@ def test_output_rounding_edge_values(h, o):
     G.compare(c, oracle_ref(o, tiny, tinyb, tgemm.BF16_BF16).view(np.int16), "bf16")
 
 
-# Regression: at the barrier that ends a K-step, reads of the current stage may still
-# be in flight while the stage's refill is issued. Refills that write zeros at once --
-# a K-tile past the end (a zero-length buffer), the lanes past K of a partial last
-# K-tile -- must wait for them (every wave waits for its LDS reads before such a
-# barrier). Without that wait, one-K-tile split-K slices run after another product
-# (which leaves data in LDS) lost the last substep of a slice in some runs. Each case
-# is repeated with a different product in between; every run must give the same bits,
-# and those must meet the accuracy rule.
+# Regression: at the barrier that ends a K-step, the last fragment reads of the current
+# stage may still be in flight (those consumed by the MFMAs after the barrier), so the
+# refill issued right after it must go to a stage no wave still reads. Refills that
+# land at once -- a K-tile past the end (a zero-length buffer), the lanes past K of a
+# partial last K-tile -- are where a violation shows: one-K-tile split-K slices run
+# after another product (which leaves data in LDS) lost the last substep of a slice in
+# some runs, with the 64x64 tile (one MFMA block row per wave, so B's last fragments
+# too are read after the barrier). Each case is repeated with a different product in
+# between; every run must give the same bits, and those must meet the accuracy rule.
 @pytest.mark.parametrize("shape,splits", [((256, 256, 4096), 64), ((256, 256, 4104), 0), ((128, 512, 2056), 8)],
                          ids=str)
 def test_refill_after_barrier_repeatable(h, o, shape, splits):
@@ -529,12 +530,14 @@ def test_odd_byte_addresses(h, o, shape, dtype):
 
 @pytest.mark.parametrize("tile", [(64, 64, 64), (128, 128, 64), (256, 128, 64), (256, 256, 64)], ids=str)
 def test_k_step_counts(h, o, tile):
-    """Stage bookkeeping at the smallest K-step counts: 1 to 6 K-tiles (full, and with a
-    partial last K-tile), 2 x 2 ragged tiles, integer-valued inputs (exact in any order):
-    every run matches the oracle bit for bit and a second run repeats it."""
+    """Stage bookkeeping at the smallest K-step counts: 1 to 13 K-tiles (every remainder
+    of the 6-step and 3-step stage cycles, before and after one or two whole cycles;
+    full, and with a partial last K-tile), 2 x 2 ragged tiles, integer-valued inputs
+    (exact in any order): every run matches the oracle bit for bit and a second run
+    repeats it."""
     tm, tn, tk = tile
     M, N = tm + 17, tn + 5
-    for nk in range(1, 7):
+    for nk in range(1, 14):
         for K in (tk * nk, tk * nk - 13):
             a = inputs.draw((M, K), "small_int", "bf16", 100 + K)
             b = inputs.draw((K, N), "small_int", "bf16", 200 + K)
@@ -552,13 +555,13 @@ def test_k_step_counts(h, o, tile):
 
 @pytest.mark.parametrize("tile", [(64, 64, 64), (128, 128, 64)], ids=str)
 def test_k_step_counts_four_stages(h, o, tile):
-    """The 4-stage twins (launches of at most 256 workgroups with 8-15 K-tiles in a multiple
-    of 4, or at least 16): K-tile counts around those thresholds, with the zero K-tiles
-    that pad the count to a multiple of 4, exact against the oracle."""
+    """The 4-stage twins (launches of at most 256 workgroups with at least 8 K-tiles per
+    slice): K-tile counts from the threshold up, every remainder of the 4-step stage
+    cycle, exact against the oracle."""
     tm, tn, tk = tile
     M, N = 2 * tm + 3, 3 * tn - 7
     seen = set()
-    for nk in (8, 12, 16, 17, 18, 19):
+    for nk in (8, 9, 10, 11, 12, 16, 17, 18, 19):
         for K in (tk * nk, tk * nk - 5):
             a = inputs.draw((M, K), "small_int", "f16", 300 + K)
             b = inputs.draw((K, N), "small_int", "f16", 400 + K)

@@ -81,26 +81,26 @@ def test_model_matches_oracle_walk(o, shape):
 
 
 def test_executed_work_and_split_workspace():
-    # 8192^3 at 256x256x64: 128 K-steps (even): no padding, executed == algorithmic
+    # 8192^3 at 256x256x64: 128 K-steps: executed == algorithmic
     m = tgemm.gemm_model(forced_plan(256, 256, 64), 8192, 8192, 8192, tgemm.BF16_BF16)
     assert m["executed_flops"] == m["flops"] and m["bytes_workspace"] == 0
     # 96^3 at tile 64: 2x2 tiles of 64x64 over K = 2 steps of 64 -> 128^2 x 128 x 2
     m = tgemm.gemm_model(forced_plan(64, 64, 64), 96, 96, 96, tgemm.BF16_F32)
     assert m["executed_flops"] == 2 * 128 * 128 * 128
-    # 3 K-steps (odd): the kernel prepends a zero K-step -> 4 steps of MFMAs
+    # 3 K-steps, the last one partial (150 = 2 x 64 + 22): 3 steps of MFMAs, no zero steps
     m = tgemm.gemm_model(forced_plan(64, 64, 64), 64, 64, 150, tgemm.BF16_F32)
-    assert m["executed_flops"] == 2 * 64 * 64 * 64 * 4
+    assert m["executed_flops"] == 2 * 64 * 64 * 64 * 3
     # split-K: 128 K-steps in 4 slices of 32; fp32 partials written and read: 2 x 4 x S x M x N
     p = auto_plan(128, 8192, 8192, tgemm.BF16_F32)
     m = tgemm.gemm_model(p, 128, 8192, 8192, tgemm.BF16_F32)
     assert p["split_k"] == 4 and m["bytes_workspace"] == 2 * 4 * 4 * 128 * 8192
     assert m["executed_flops"] == m["flops"]
-    # 4 stages: 18 K-steps padded with 2 zero K-steps to 20
+    # 4 stages: 18 K-steps, whatever the stage count
     m = tgemm.gemm_model(forced_plan(128, 128, 64, stages=4), 1792, 1792, 1096, tgemm.BF16_BF16)
-    assert m["executed_flops"] == 2 * (14 * 128) ** 2 * 64 * 20
-    # 7 K-steps in slices of 3, 3, 1 -> each odd slice gets a zero step: 4 + 4 + 2 = 10 steps
+    assert m["executed_flops"] == 2 * (14 * 128) ** 2 * 64 * 18
+    # 7 K-steps in slices of 3, 3, 1: 7 steps in all
     m = tgemm.gemm_model(forced_plan(64, 64, 64, split_k=3), 64, 64, 7 * 64, tgemm.BF16_F32)
-    assert m["executed_flops"] == 2 * 64 * 64 * 64 * 10
+    assert m["executed_flops"] == 2 * 64 * 64 * 64 * 7
 
 
 def test_model_rejects_bad_plans():
@@ -116,25 +116,24 @@ def test_model_rejects_bad_plans():
 
 def test_model_of_a_tail_split():
     """executed_flops and the workspace of a plan with a split-K tail: the tiles of
-    rows [0, tail_m0) over the whole K range, each tail tile in S slices, each slice
-    (and the whole range) padded with zero K-tiles to a multiple of the stage count."""
+    rows [0, tail_m0) over the whole K range, each tail tile in S slices that
+    together cover the same K-tiles."""
     for M, N, K, dtype in [(6000, 6000, 6000, tgemm.BF16_BF16), (4352, 4096, 1024, tgemm.BF16_F32),
                            (7000, 7000, 7000, tgemm.F16_F16)]:
         p = auto_plan(M, N, K, dtype)
         assert p["tail_split_k"] > 1
         m = tgemm.gemm_model(p, M, N, K, dtype)
-        tm, tn, tk, S, ns = p["tile_m"], p["tile_n"], p["tile_k"], p["tail_split_k"], p["stages"]
+        tm, tn, tk, S = p["tile_m"], p["tile_n"], p["tile_k"], p["tail_split_k"]
         nk = -(-K // tk)
 
-        def padded_steps(splits):
+        def slice_steps(splits):
             per = -(-nk // splits)
-            sizes = [min(per, nk - lo) for lo in range(0, nk, per)]
-            return sum(n + (-n) % ns for n in sizes)
+            return sum(min(per, nk - lo) for lo in range(0, nk, per))
 
         tiles_n = -(-N // tn)
         main_tiles = (p["tail_m0"] // tm) * tiles_n
         tail_tiles = (-(-M // tm)) * tiles_n - main_tiles
-        want = 2 * tm * tn * tk * (main_tiles * padded_steps(1) + tail_tiles * padded_steps(S))
+        want = 2 * tm * tn * tk * (main_tiles * slice_steps(1) + tail_tiles * slice_steps(S))
         assert m["executed_flops"] == want
         copies = (4 * M * K if p["repack"] & 1 else 0) + (4 * K * N if p["repack"] & 2 else 0)  # read + write
         assert m["bytes_workspace"] == 8 * S * (M - p["tail_m0"]) * N + copies

@@ -73,7 +73,7 @@ constexpr int64_t kSplitMinKTiles = 32;      // automatic split-K only for long 
 constexpr int kMaxTuneIters = 1000;                      // timed launches per candidate, at most
 constexpr int64_t kTuneMaxWorkgroups = 8192;             // split candidates beyond this many workgroups are skipped
 constexpr int64_t kTuneSmallTileMaxOutputs = 1 << 20;    // the 16x16x32 tile is tried for outputs up to this size
-constexpr int64_t kDeepMinKTiles = 16;       // per K-slice, so the zero K-tiles padding a slice stay few
+constexpr int64_t kDeepMinKTiles = 8;        // per K-slice: shorter slices gain nothing from more loads in flight
 // Cost figures of the tail split (MI355X, bf16): one K-step of a round of 256x256 tiles,
 // and the rate at which the split-K partial tiles are written and read back.
 constexpr double kStepSeconds = 1.55e-6;
@@ -370,11 +370,10 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
     if (sk >= 2) p.split_k = (int32_t)cdiv(nk, cdiv(nk, sk));
     // Deeper pipeline: when the launch leaves at most one workgroup per compute unit
     // (so no other workgroup hides a workgroup's memory latency) and each K-slice is
-    // long (or a multiple of 4 K-tiles, so that no zero tile pads it), the 4-stage
-    // twin of the tile keeps three K-tiles of loads in flight.
+    // at least kDeepMinKTiles long, the 4-stage twin of the tile keeps three K-tiles of
+    // loads in flight.
     const int64_t nk_slice = cdiv(nk, p.split_k);
-    if (p.kernel == 4 && p.vector_loads && p.grid * p.split_k <= kDeepMaxWorkgroups &&
-        (nk_slice >= kDeepMinKTiles || (nk_slice >= 8 && nk_slice % 4 == 0))) {
+    if (p.kernel == 4 && p.vector_loads && p.grid * p.split_k <= kDeepMaxWorkgroups && nk_slice >= kDeepMinKTiles) {
       const int deep = find_macro(p.tile_m, p.tile_n, p.tile_k, 4);
       if (deep >= 0) {
         p.stages = 4;
@@ -803,33 +802,11 @@ gemm_status_t gemm_model(const gemm_plan_t* plan, int64_t M, int64_t N, int64_t 
     const double tile_mn = (double)p.tile_m * p.tile_n * (double)m.tiles;
     if (p.kernel == 2) {
       m.executed_flops = 2.0 * tile_mn * dK;  // every thread of a tile runs the actual K range
-    } else if (p.kernel == 3) {
-      m.executed_flops = 2.0 * tile_mn * (double)(nk * p.tile_k);
     } else {
-      // per K-slice: its K-tiles, plus the zero K-tiles prepended to make their number
-      // a multiple of the stage count
-      const int64_t ns = p.stages > 0 ? p.stages : 2;
-      auto slice_steps = [&](int64_t splits) {
-        const int64_t per = cdiv(nk, splits);
-        double steps = 0;
-        for (int64_t lo = 0; lo < nk; lo += per) {
-          const int64_t n = (nk - lo) < per ? (nk - lo) : per;
-          steps += (double)(n + (ns - n % ns) % ns);
-        }
-        return steps;
-      };
-      const bool tail = p.tail_split_k > 1 && p.tail_m0 > 0 && p.tail_m0 < M;
-      if (tail) {
-        // the tiles of rows [0, tail_m0) over the whole K range, the tail's tiles in slices
-        const double tiles_main = (double)(cdiv(p.tail_m0, p.tile_m) * tn);
-        const double tiles_tail = (double)m.tiles - tiles_main;
-        const double tile_elems = (double)p.tile_m * p.tile_n;
-        m.executed_flops =
-            2.0 * tile_elems * p.tile_k * (tiles_main * slice_steps(1) + tiles_tail * slice_steps(p.tail_split_k));
+      // every tile runs its K-tiles (split into K-slices or not), the last one zero-padded
+      m.executed_flops = 2.0 * tile_mn * (double)(nk * p.tile_k);
+      if (p.kernel == 4 && p.tail_split_k > 1 && p.tail_m0 > 0 && p.tail_m0 < M)
         m.bytes_workspace = 2.0 * 4.0 * (double)p.tail_split_k * (double)(M - p.tail_m0) * dN;
-      } else {
-        m.executed_flops = 2.0 * tile_mn * slice_steps(p.split_k) * p.tile_k;
-      }
     }
     if (p.split_k > 1) m.bytes_workspace = 2.0 * 4.0 * (double)p.split_k * dM * dN;
     // operand copies: each flagged operand read and written once

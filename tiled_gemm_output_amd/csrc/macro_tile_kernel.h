@@ -18,10 +18,13 @@
 // gfx950 design (differs from the pages' one-thread-per-element kernels):
 //  * waves of 64 lanes, each owning a (BM/WM) x (BN/WN) sub-tile computed with
 //    v_mfma_f32_32x32x16_{bf16,f16};
-//  * NS LDS stages (2 by default: the loads of step k+1 are in flight while step k
-//    is multiplied; 4 for launches with at most one workgroup per compute unit,
-//    where more loads in flight hide memory latency that other workgroups cannot),
-//    one barrier per step;
+//  * a pipeline of LDS stages with one barrier per K-step: K-tile kt lives in A
+//    stage kt % NA and B stage kt % NB and is loaded D steps before it is
+//    multiplied (D = 2 with three A stages and two B stages by default; D = 3 with
+//    four of each for launches with at most one workgroup per compute unit, where
+//    more loads in flight hide memory latency that other workgroups cannot). A
+//    stage is only ever refilled once every wave's reads of it have completed
+//    (see the main loop);
 //  * vector path (A and B at even addresses: any shape and leading dimension):
 //    16-byte buffer loads straight from global memory into LDS (buffer_load_dwordx4
 //    ... lds), no register staging; out-of-range lanes use an offset beyond the
@@ -44,6 +47,10 @@
 
 namespace tg {
 
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+
+// NS names the pipeline: 2 = K-tiles loaded two steps ahead into three A stages and
+// two B stages; 4 = loaded three steps ahead into four stages of each.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int NS_ = 2>
 struct MacroCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, NS = NS_;
@@ -53,9 +60,23 @@ struct MacroCfg {
   static constexpr int kFM = kWTM / 32, kFN = kWTN / 32;  // 32x32 MFMA blocks per wave
   static constexpr int kABytes = BM * BK * 2, kBBytes = BK * BN * 2;
   static constexpr int kSubsteps = BK / 16;
-  static constexpr int kLds = NS * (kABytes + kBBytes);
+  static constexpr int D = NS == 2 ? 2 : NS - 1;  // K-steps between a K-tile's load and its use
+  // The last substep's MFMAs are split around the step's barrier: block rows
+  // [0, kFM / 2) before it, the rest after. B's fragments are all consumed before
+  // the barrier when that first half is not empty (kFM >= 2).
+  static constexpr bool kBDoneAtBarrier = kFM >= 2;
+  static constexpr int NA = NS == 2 ? 3 : NS;                              // A stages
+  static constexpr int NB = NS == 2 ? (kBDoneAtBarrier ? 2 : 3) : NS;      // B stages
+  static constexpr int L = NA / gcd_c(NA, NB) * NB;  // steps after which the stage pattern repeats
+  static constexpr int kLds = NA * kABytes + NB * kBBytes;
   static_assert(BK == 64, "four 16-deep substeps per K-step");
-  static_assert(NS >= 2 && NS <= 4, "2 to 4 LDS stages");
+  static_assert(NS == 2 || NS == 4, "two pipelines");
+  // The refill of K-tile st + D, issued right after step st's barrier, must not land
+  // in a stage that is still to be read: the stages of st + 1 .. st + D - 1, and the
+  // stage of st itself unless every wave consumed its last reads of it before the
+  // barrier (B when kBDoneAtBarrier; never A).
+  static_assert(D >= 2 && NA >= D + 1 && NB >= D + (kBDoneAtBarrier ? 0 : 1),
+                "refill targets a stage no wave still reads");
   static_assert(kFM >= 1 && kFN >= 1 && kWTM % 32 == 0 && kWTN % 32 == 0, "wave tile must be a multiple of 32x32");
   static_assert(kLds <= 160 * 1024, "LDS budget");
 };
@@ -182,6 +203,13 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<I + 1, N>(f);
   }
 }
+// f(IC<I>), then f(IC<I + 1>) only if it returned true, and so on.
+template <int I, int N, class F>
+__device__ __forceinline__ void nested_for(F&& f) {
+  if constexpr (I < N) {
+    if (f(IC<I>{})) nested_for<I + 1, N>(f);
+  }
+}
 
 // Workgroup barrier without a memory fence. The waits the pipeline needs are
 // explicit s_waitcnt instructions placed before it (a fenced barrier would also
@@ -226,8 +254,8 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   constexpr int kAPer = OA::kPer, kBPer = OB::kPer;
   constexpr int NR = FM * OA::kReads + FN * OB::kReads;  // LDS reads per substep
   constexpr int NM = FM * FN;                            // MFMAs per substep
-  constexpr int NS = Cfg::NS;
-  static_assert(VEC || NS == 2, "the element loader stages one K-tile ahead in registers: two LDS stages");
+  constexpr int NA = Cfg::NA, NB = Cfg::NB, D = Cfg::D, L = Cfg::L;
+  static_assert(VEC || Cfg::NS == 2, "the element loader stages one K-tile ahead in registers");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -240,7 +268,8 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   const int row0 = tile_m * BM, col0 = tile_n * BN;
   const int M = p.M, N = p.N, K = p.K;
   const int64_t lda = p.lda, ldb = p.ldb;
-  // K-tiles of this workgroup: [kt_base, kt_base + nk) (all of them without split-K)
+  // K-tiles of this workgroup: [kt_base, kt_base + nk) (all of them without split-K);
+  // below, K-tile indices kt count from kt_base
   const int kt_base = blockIdx.y * p.kt_per_split;
   const int nk_all = (K + BK - 1) / BK;
   const int nk = (nk_all - kt_base) < p.kt_per_split ? (nk_all - kt_base) : p.kt_per_split;
@@ -280,7 +309,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   // Vector path: issue the direct loads of K-tile kt into a stage. Branch-free: a
   // K-tile outside [0, nk) gets a zero-length buffer, so every lane reads zeros and
   // no memory is touched (this keeps the compiler's tracking of which stage each
-  // load writes exact, so it adds no waits before reads of the other stage).
+  // load writes exact, so it adds no waits before reads of the other stages).
   // Loads are whole 16-byte chunks at 2-byte alignment: a chunk that runs past the
   // end of a stored row reads the start of the next row (or its padding), which lands
   // at positions past M or N (outputs that are never stored) or past K (cleared once
@@ -289,10 +318,6 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   // zeros. With an odd stored row length (K for a K-contiguous operand, M or N
   // otherwise) the dword holding the matrix's last element also covers two bytes past
   // the end, so that element reads as zero too; it is written into LDS afterwards.
-  const bool a_odd = ((TA ? M : K) & 1) != 0, b_odd = ((TB ? K : N) & 1) != 0;
-  // 1 when the refill of the last K-tile writes zeros at positions that hold data
-  // (a partial K-tile, or the matrix's last element)
-  const int late_zero = (LOAD == kLoadVec || a_odd || b_odd) ? 1 : 0;
   auto issue_loads = [&](TG_LDS char* sa, TG_LDS char* sb, int kt) __attribute__((always_inline)) {
     const bool ok = (unsigned)kt < (unsigned)nk;
     const int k0 = ok ? (kt_base + kt) * BK : 0;
@@ -443,26 +468,43 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
         for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<IN>(b[j], a[i], acc[i][j]);
   };
 
-  TG_LDS char* pA[NS];
-  TG_LDS char* pB[NS];
-  static_for<0, NS>([&](auto i) {
-    pA[i.value] = lds_stage<0, i.value, Cfg::kABytes>();
-    pB[i.value] = lds_stage<1, i.value, Cfg::kBBytes>();
-  });
+  TG_LDS char* pA[NA];
+  TG_LDS char* pB[NB];
+  static_for<0, NA>([&](auto i) { pA[i.value] = lds_stage<0, i.value, Cfg::kABytes>(); });
+  static_for<0, NB>([&](auto i) { pB[i.value] = lds_stage<1, i.value, Cfg::kBBytes>(); });
 
   // ---------------- main loop ----------------
-  // NS stages; K-tile kt0 + st lives in stage st % NS. Each step multiplies its
-  // stage in four substeps; the reads of substep s+1 are issued among the MFMAs
-  // of substep s. The barrier that ends the step sits after the first half of the
-  // last substep's MFMAs: once every wave is past it, the stage just consumed is
-  // refilled with K-tile st + NS and the next stage's first fragments are read,
-  // both covered by the second half of those MFMAs. Before the barrier each wave
-  // waits until its loads of K-tile st + 1 have landed (those of the NS - 2 later
-  // K-tiles may still be in flight). Zero K-tiles (indices below 0) are prepended
-  // so that the number of steps is a multiple of NS and every step is unconditional.
+  // K-tile kt lives in A stage kt % NA and B stage kt % NB. Step st multiplies
+  // K-tile st in four substeps; the reads of substep s+1 are issued among the MFMAs
+  // of substep s. The step's barrier sits after the first half of the last
+  // substep's MFMAs: before it each loading wave waits until its loads of K-tile
+  // st + 1 have landed (those of K-tiles st + 2 .. st + D - 1 may still be in
+  // flight); right after it K-tile st + D is loaded and the first fragments of
+  // K-tile st + 1 are read, both covered by the second half of those MFMAs.
+  //
+  // Why no stage is written while a wave may still read it ("Tiled Matrix
+  // Multiplication", section 5: a barrier after the tile is consumed, before it
+  // is overwritten). A wave's LDS read is complete once the wave has waited for
+  // its result (s_waitcnt lgkmcnt, which the compiler places before the MFMA
+  // that consumes it). Step st's reads of K-tile st end with the last substep's
+  // fragments, consumed by MFMAs before step st's barrier (B's, when kFM >= 2)
+  // or right after it, so before step st + 1's barrier. The refill of K-tile
+  // st + D is issued after step st's barrier into the stage that held K-tile
+  // st + D - NA (A) or st + D - NB (B): st - 1 or earlier (NA >= D + 1), all of
+  // whose reads every wave completed before step st's barrier; or, for B when
+  // kFM >= 2, possibly st itself (NB >= D), whose B reads are also complete
+  // before that barrier. The writes before step st's barrier (the element
+  // loader's K-tile st + 1, the clean-up of a last K-tile) go to the stages of
+  // K-tile st + 1, which held K-tile st + 1 - NA <= st - 2 (A) and st + 1 - NB
+  // (B: st - 2, or st - 1 when kFM >= 2), whose reads every wave completed before
+  // step st - 1's barrier, which every wave has passed. (The fragments read after
+  // the last step, from the stage of a K-tile past the slice, are never
+  // multiplied.)
+  //
+  // The stage pattern repeats every L steps: the loop body is one cycle of L
+  // unrolled steps (stage indices are compile-time, so the compiler tracks the
+  // direct loads of each stage apart), and the last nk % L steps follow it.
   constexpr int PER = kAPer + kBPer;  // direct loads per wave and K-tile
-  const int kt0 = -((NS - nk % NS) % NS);
-  const int nsteps = nk - kt0;  // a multiple of NS, >= NS
   i32x4 fa[FM], fb[FN], ga[FM], gb[FN];
   // The pipeline, for a wave that loads (LOADER) or one that only multiplies; the
   // two are separate branch-free copies, so the compiler tracks each one's loads
@@ -472,23 +514,25 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
     constexpr bool LOADER = decltype(ROLE)::value != 0;
     if constexpr (VEC) {
       if constexpr (LOADER) {
-        static_for<0, NS>([&](auto i) { issue_loads(pA[i.value], pB[i.value], kt0 + i.value); });
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (NS - 1)));  // K-tile kt0 landed
-        fix_last(pA[0], pB[0], kt0);
+        static_for<0, D>([&](auto i) { issue_loads(pA[i.value % NA], pB[i.value % NB], i.value); });
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (D - 1)));  // K-tile 0 landed
+        fix_last(pA[0], pB[0], 0);
       }
     } else {
-      fetch_regs(kt0);
+      fetch_regs(0);
       store_regs(pA[0], pB[0]);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     }
     barrier_nofence();
-    if constexpr (!VEC) fetch_regs(kt0 + 1);
+    if constexpr (!VEC) fetch_regs(1);
     read_frags(pA[0], pB[0], 0, fa, fb);
 
     auto step = [&](auto J, int st) __attribute__((always_inline)) {
-      constexpr int cur = decltype(J)::value, nxt = (cur + 1) % NS;
-      TG_LDS char* const sa = pA[cur];
-      TG_LDS char* const sb = pB[cur];
+      constexpr int j = decltype(J)::value;
+      TG_LDS char* const sa = pA[j % NA];  // K-tile st
+      TG_LDS char* const sb = pB[j % NB];
+      TG_LDS char* const na = pA[(j + 1) % NA];  // K-tile st + 1
+      TG_LDS char* const nb = pB[(j + 1) % NB];
       read_frags(sa, sb, 1, ga, gb);
       mfma_rows(fa, fb, 0, FM);
       interleave<NM, NR, 0>();
@@ -503,37 +547,39 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
       __builtin_amdgcn_sched_barrier(0);
       mfma_rows(ga, gb, 0, FM / 2);
       __builtin_amdgcn_sched_barrier(0);
-      // The next stage must be complete in every wave before anyone reads it.
+      // K-tile st + 1 must be complete in every wave before anyone reads it.
       if constexpr (VEC) {
         if constexpr (LOADER) {
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (NS - 2)));  // its loads of K-tile st + 1 landed
-          fix_last(pA[nxt], pB[nxt], kt0 + st + 1);
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (D - 2)));  // its loads of K-tile st + 1 landed
+          fix_last(na, nb, st + 1);
         }
-        // Right after this barrier the current stage is refilled while reads of it
-        // (the last substep's fragments) may still be in flight. A refill from memory
-        // lands long after they complete, and lanes outside M or N write zeros where
-        // only unused data lies; but a K-tile past the end (a zero-length buffer), the
-        // lanes past K of a partial last K-tile and the zeroed last element of the
-        // matrix are written at once, over data still being read. Before those
-        // refills every wave first waits for its LDS reads.
-        if ((kt0 + st + NS) >= nk - late_zero) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       } else {
-        store_regs(pA[nxt], pB[nxt]);        // K-tile st + 1, fetched one step ago
+        store_regs(na, nb);                  // K-tile st + 1, fetched one step ago
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       }
       barrier_nofence();
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (VEC && LOADER)
-        issue_loads(sa, sb, kt0 + st + NS);  // beyond the last K-tile: zero-length, no traffic
-      else
-        fetch_regs(kt0 + st + 2);
-      read_frags(pA[nxt], pB[nxt], 0, fa, fb);
+        issue_loads(pA[(j + D) % NA], pB[(j + D) % NB], st + D);  // past the last K-tile: zero-length, no traffic
+      else if constexpr (!VEC)
+        fetch_regs(st + 2);
+      read_frags(na, nb, 0, fa, fb);
       mfma_rows(ga, gb, FM / 2, FM);
       interleave<(FM - FM / 2) * FN, NR, (VEC && LOADER) ? PER : 0>();
       __builtin_amdgcn_sched_barrier(0);
     };
-    for (int st = 0; st < nsteps; st += NS) static_for<0, NS>([&](auto J) { step(J, st + J.value); });
-};
+    int st = 0;
+    for (; st + L <= nk; st += L) static_for<0, L>([&](auto J) { step(J, st + J.value); });
+    // The remaining nk % L steps, nested so that a skipped step leads only to the
+    // end: a path that skipped a step never reaches a later one, so the compiler
+    // keeps an exact account of which stage each load in flight writes (a join
+    // that let it would make it wait for every load before the next fragment reads).
+    nested_for<0, L - 1>([&](auto J) __attribute__((always_inline)) {
+      if (st + J.value >= nk) return false;
+      step(J, st + J.value);
+      return true;
+    });
+  };
   if constexpr (LW == Cfg::kWaves)
     run(IC<1>{});
   else if (wave < LW)
@@ -562,15 +608,17 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
     constexpr int CH = RB / 16;         // 16-byte chunks per row
     constexpr int SLICE = 32 * RB;      // one block row
     constexpr int PER_OBJ = Cfg::kABytes / SLICE;
-    static_assert(CH >= 2 && 64 % CH == 0 && PER_OBJ >= 1 && Cfg::kWaves <= NS * PER_OBJ,
+    static_assert(CH >= 2 && 64 % CH == 0 && PER_OBJ >= 1 && Cfg::kWaves <= NA * PER_OBJ,
                   "the wave slices fit in the A stages");
     // every wave is done with the stages, and no direct load is still landing
     __builtin_amdgcn_s_waitcnt(0);
     barrier_nofence();
-    TG_LDS char* slice = pA[0];
-    static_for<0, NS>([&](auto S) {
-      if (wave / PER_OBJ == S.value) slice = pA[S.value] + (wave % PER_OBJ) * SLICE;
-    });
+    // wave w's slice: number w % PER_OBJ of A stage w / PER_OBJ (two-way choice at
+    // most: an indexed choice among the stages would go through scratch memory)
+    constexpr int NOBJ = (Cfg::kWaves + PER_OBJ - 1) / PER_OBJ;
+    static_assert(NOBJ <= 2, "wave slices span at most two A stages");
+    TG_LDS char* const slice =
+        (NOBJ == 1 || wave < PER_OBJ ? pA[0] : pA[NOBJ - 1]) + (wave % PER_OBJ) * SLICE;
     const int r = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
