@@ -67,7 +67,7 @@ typedef enum TGEMM_ENUM_BASE {
   GEMM_ERR_NO_DEVICE = 3,         /* no HIP device visible */
   GEMM_ERR_ARCH = 4,              /* current device is not gfx950 */
   GEMM_ERR_HIP = 5,               /* a HIP runtime call or kernel launch failed */
-  GEMM_ERR_OUT_OF_MEMORY = 6,     /* allocation of the handle or of its split-K workspace failed */
+  GEMM_ERR_OUT_OF_MEMORY = 6,     /* a host allocation, or a device workspace allocation, failed */
   GEMM_ERR_UNSUPPORTED_TILE = 7   /* gemm_set_tile asked for a tile no kernel has, for this dtype */
 } gemm_status_t;
 
@@ -158,12 +158,14 @@ gemm_status_t gemm_create(gemm_handle_t* out);
  * and a last, partly full round of tiles may run as a split-K tail (tail_split_k).
  * The fp32 partial tiles go to a device workspace owned by the handle; operand
  * copies into line-aligned rows (gemm_plan reports repack; see gemm_set_repack) go
- * to a second one. Each is allocated (hipMalloc) on the first call that needs it,
- * grown when a later call needs more (the old one is freed, which waits for work
- * still using it), and freed by gemm_destroy. Calls on one handle that use a
+ * to a second one. Each is allocated (hipMalloc) by the first call that needs it and
+ * replaced by a larger one when a later call needs more; a replaced buffer is kept
+ * (work enqueued or captured earlier may still use it) until gemm_destroy frees them
+ * all. Such a call is the one case where gemm_run allocates device memory, and
+ * hipMalloc may synchronize with the device. Calls on one handle that use a
  * workspace share it, so they must be ordered (one stream, or synchronized between
- * streams). Partial sums are added in a fixed order, so results are reproducible
- * run to run.
+ * streams); use one handle per stream otherwise. Partial sums are added in a fixed
+ * order, so results are reproducible run to run.
  * Stream capture: a call only enqueues kernels on `stream` (no memset, no
  * synchronization), so it may be captured into a HIP graph, provided the handle's
  * workspace is already large enough: a captured call that would have to allocate or
@@ -207,8 +209,8 @@ gemm_status_t gemm_tune(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t
                         const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                         gemm_dtype_t dtype, void* stream, int32_t iters, gemm_plan_t* best);
 
-/* Release a handle and its workspaces (hipFree waits for work still using them).
- * NULL or an already destroyed handle -> GEMM_ERR_INVALID_ARG. */
+/* Release a handle and its workspaces, replaced ones included (hipFree waits for work
+ * still using them). NULL or an already destroyed handle -> GEMM_ERR_INVALID_ARG. */
 gemm_status_t gemm_destroy(gemm_handle_t h);
 
 /* Force the C tile (tm x tn) and K-step tk of later gemm_run calls on this handle;

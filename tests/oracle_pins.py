@@ -214,6 +214,38 @@ def check_encode_f16(o, seed=3):
     assert np.array_equal(got, ref), int(np.sum(got != ref))
 
 
+def check_encode_special(o):
+    """Non-finite values and signed zeros: NaN stays NaN (the quiet NaN with the
+    input's sign), infinities keep their sign, -0.0 stays -0.0, in every output
+    format. Expected bits from numpy's binary64 -> binary16 / binary32 conversions;
+    for bfloat16, the upper half of the binary32 pattern (bfloat16 is binary32's
+    upper half, and these values need no rounding)."""
+    x = np.array([np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0])
+    with np.errstate(invalid="ignore"):
+        f32 = x.astype(np.float32).view(np.uint32)
+        want = {
+            "f16": x.astype(np.float16).view(np.uint16),
+            "f32": f32,
+            "bf16": (f32 >> 16).astype(np.uint16),
+        }
+    # the patterns themselves: quiet NaN, infinity and zero of each format, sign bit set for the negatives
+    assert [hex(v) for v in want["f16"]] == ["0x7e00", "0xfe00", "0x7c00", "0xfc00", "0x0", "0x8000"]
+    assert [hex(v) for v in want["f32"]] == ["0x7fc00000", "0xffc00000", "0x7f800000", "0xff800000", "0x0",
+                                             "0x80000000"]
+    assert [hex(v) for v in want["bf16"]] == ["0x7fc0", "0xffc0", "0x7f80", "0xff80", "0x0", "0x8000"]
+    for kind, ref in want.items():
+        got = o.encode(x, kind)
+        assert np.array_equal(got, ref), (kind, [hex(v) for v in got], [hex(v) for v in ref])
+    # an infinite or NaN input flows through the product as in IEEE binary64
+    a = np.array([[np.inf, 1.0], [np.nan, 0.0], [1.0, -0.0]])
+    b = np.array([[2.0], [3.0]])
+    for kind, enc in (("bf16", "bf16"), ("f16", "f16")):
+        ab = np.asarray(o.encode(a.ravel(), enc), dtype=np.uint16).reshape(a.shape)
+        bb = np.asarray(o.encode(b.ravel(), enc), dtype=np.uint16).reshape(b.shape)
+        c = o.gemm(ab, bb, kind, "f32").astype(np.float64)
+        assert c[0, 0] == np.inf and np.isnan(c[1, 0]) and c[2, 0] == 2.0, c
+
+
 def check_encode_f32(o, seed=4):
     rng = np.random.default_rng(seed)
     x = np.ldexp(rng.random(20000) + 0.5, rng.integers(-160, 135, size=20000))
@@ -367,6 +399,7 @@ def check_counts(o, seed=51):
 
 ALL_CHECKS = [
     check_worked_example,
+    check_encode_special,
     check_bruteforce_int,
     check_bruteforce_float,
     check_decode_exhaustive,

@@ -95,3 +95,44 @@ def test_graph_replays_match_eager(o, case):
             assert np.array_equal(got, eager), "replay %d differs from the eager result" % r
     finally:
         tgemm.gemm_destroy(h)
+
+
+def test_graph_replay_after_workspace_growth(o):
+    """A captured split-K call keeps the workspace it was captured with: a later eager
+    call on the same handle that needs a larger one gets a new buffer (the old one is
+    kept until gemm_destroy), so every replay still reproduces the eager result."""
+    dtype = tgemm.BF16_F32
+    (Ms, Ns, Ks), (Mb, Nb, Kb) = (128, 2048, 4096), (128, 8192, 8192)  # 4 and 16 MiB of fp32 partial tiles
+    a, b = _inputs(Ms, Ns, Ks, dtype, 5)
+    xa, xb = _inputs(Mb, Nb, Kb, dtype, 6)
+    da, db = torch.from_numpy(a.view(np.int16)).cuda(), torch.from_numpy(b.view(np.int16)).cuda()
+    dxa, dxb = torch.from_numpy(xa.view(np.int16)).cuda(), torch.from_numpy(xb.view(np.int16)).cuda()
+    dc = torch.zeros((Ms, Ns), dtype=torch.int32, device="cuda")
+    dxc = torch.zeros((Mb, Nb), dtype=torch.int32, device="cuda")
+    h = tgemm.gemm_create()
+    try:
+        tgemm.check(tgemm.gemm_set_split_k(h, 4))
+
+        def small(stream):
+            tgemm.check(tgemm.gemm_run(h, Ms, Ns, Ks, da.data_ptr(), Ks, db.data_ptr(), Ns, dc.data_ptr(), Ns, dtype,
+                                       stream))
+
+        small(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        eager = dc.cpu().numpy().copy()
+        G.compare(eager, o.gemm(a, b, "bf16", "f32").view(np.int32), "f32")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            small(torch.cuda.current_stream().cuda_stream)
+        for r in range(3):
+            # needs a larger workspace than the captured call's
+            tgemm.check(tgemm.gemm_run(h, Mb, Nb, Kb, dxa.data_ptr(), Kb, dxb.data_ptr(), Nb, dxc.data_ptr(), Nb,
+                                       dtype, torch.cuda.current_stream().cuda_stream))
+            dc.zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(dc.cpu().numpy(), eager), "replay %d differs from the eager result" % r
+        G.compare(dxc.cpu().numpy(), o.gemm(xa, xb, "bf16", "f32").view(np.int32), "f32")
+    finally:
+        tgemm.gemm_destroy(h)

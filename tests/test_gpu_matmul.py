@@ -100,3 +100,29 @@ def test_matmul_rejects_strided_views():
     a = torch.zeros(64, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         matmul(a[:, ::2], a[:32])
+
+
+def test_matmul_split_k_on_two_streams(o):
+    """Two split-K products (each tile's K range in slices whose fp32 partial tiles go
+    to a workspace) enqueued on two streams with no synchronization between them:
+    each stream's calls go through a handle of their own, so neither overwrites the
+    other's partial tiles. Both results match the oracle."""
+    M, N, K = 128, 8192, 8192
+    p = tgemm.gemm_plan(None, M, N, K, 1 << 20, K, 1 << 30, N, 1 << 34, N, tgemm.BF16_F32)
+    assert p["split_k"] > 1, p
+    cases = [inputs.random_case(M, N, K, "bf16", seed=s) for s in (11, 12)]
+    d = [(dev(a, "bf16"), dev(b, "bf16")) for a, b in cases]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            c1 = matmul(*d[0], out_dtype=torch.float32)
+        with torch.cuda.stream(s2):
+            c2 = matmul(*d[1], out_dtype=torch.float32)
+        outs.append((c1, c2))
+    torch.cuda.synchronize()
+    refs = [o.gemm(a, b, "bf16", "f32").view(np.int32) for a, b in cases]
+    for c1, c2 in outs:
+        G.compare(host_bits(c1), refs[0], "f32")
+        G.compare(host_bits(c2), refs[1], "f32")

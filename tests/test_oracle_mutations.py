@@ -31,6 +31,10 @@ MUTATIONS = {
     "ties_away": ("double r = nearbyint(ldexp(ax, -q));", "double r = round(ldexp(ax, -q));"),
     "double_rounding": ("double r = nearbyint(ldexp(ax, -q));", "double r = nearbyint(ldexp((double)(float)ax, -q));"),
     "no_subnormals": ("if (lead < emin) lead = emin;", "if (0) lead = emin;"),
+    "nan_encoded_as_inf": ("if (isnan(x)) return sign_bit | (exp_all << fbits) | (1u << (fbits - 1));",
+                           "if (isnan(x)) return sign_bit | (exp_all << fbits);"),
+    "inf_sign_dropped": ("if (isinf(x)) return sign_bit | (exp_all << fbits);", "if (isinf(x)) return exp_all << fbits;"),
+    "negative_zero_dropped": ("if (ax == 0.0) return sign_bit;", "if (ax == 0.0) return 0;"),
     # counts
     "ops_halved": ("return 2 * M * N * K;", "return M * N * K;"),
     "traffic_padded_rows": ("int64_t rows = padded ? tm : m1 - m0;", "int64_t rows = tm;"),
@@ -40,7 +44,7 @@ MUTATIONS = {
 }
 
 # cheap pins first; the child stops at the first failure
-ORDER = ["check_counts", "check_worked_example", "check_special_cases", "check_sampled_and_strided",
+ORDER = ["check_counts", "check_worked_example", "check_encode_special", "check_special_cases", "check_sampled_and_strided",
          "check_against_numpy_matmul", "check_encode_f32", "check_encode_f16", "check_encode_bf16",
          "check_decode_exhaustive", "check_bruteforce_int", "check_bruteforce_float"]
 

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <new>
 #include <unordered_map>
@@ -37,20 +38,68 @@ struct tune_choice {
   int tail_split_k = 0, tail_m0 = 0;  // a split-K tail after the full rounds (the automatic plan's)
 };
 
+// Device memory a call's kernels may use besides A, B and C: the fp32 partial tiles
+// of split-K (WS_SPLIT) and operand copies into aligned rows (WS_PACK).
+enum WsKind { WS_SPLIT = 0, WS_PACK = 1 };
+
 struct tgemm_handle {
   int device;
   int cus;
   int tm, tn, tk;   // forced tile, 0 = automatic
   int splits;       // forced K-slice count, 0 = automatic
   int repack;       // operand copies: 0 automatic, 1 always (rows not 16-byte aligned), -1 never
-  void* ws;         // split-K workspace (device memory owned by the handle), or null
-  size_t ws_bytes;  // its size
-  void* pack;       // workspace of operand copies (device memory owned by the handle), or null
-  size_t pack_bytes;
+  void* ws[2];          // the handle's workspaces (device memory it owns), by WsKind, or null
+  size_t ws_bytes[2];   // their sizes
+  std::vector<void*> retired;  // workspaces replaced by larger ones, freed by gemm_destroy
   std::unordered_map<tune_key, tune_choice, tune_key_hash> tuned;  // gemm_tune results
 };
 
 namespace {
+
+// Where a call's workspace comes from.
+struct WsSource {
+  // at least `bytes` of device memory of that kind, 256-byte aligned, or nullptr with *st set
+  virtual void* get(WsKind kind, size_t bytes, gemm_status_t* st) = 0;
+
+ protected:
+  ~WsSource() = default;
+};
+
+// The handle's workspaces: allocated by the first call that needs one and replaced by a
+// larger one when a later call needs more. A replaced buffer is not freed before
+// gemm_destroy: work enqueued earlier, or captured into a graph, may still use it (and
+// hipFree would wait for the device).
+struct HandleWs final : WsSource {
+  tgemm_handle* h;
+  explicit HandleWs(tgemm_handle* hh) : h(hh) {}
+  void* get(WsKind kind, size_t bytes, gemm_status_t* st) override {
+    if (h->ws_bytes[kind] >= bytes) return h->ws[kind];
+    h->retired.reserve(h->retired.size() + 1);  // may throw before anything is allocated
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      *st = GEMM_ERR_OUT_OF_MEMORY;
+      return nullptr;
+    }
+    if (h->ws[kind] != nullptr) h->retired.push_back(h->ws[kind]);
+    h->ws[kind] = p;
+    h->ws_bytes[kind] = bytes;
+    return p;
+  }
+};
+
+// Runs an entry point's body; no C++ exception leaves the C interface: an allocation
+// failure is GEMM_ERR_OUT_OF_MEMORY, anything else GEMM_ERR_HIP.
+template <class F>
+gemm_status_t guarded(F&& f) noexcept {
+  try {
+    return f();
+  } catch (const std::bad_alloc&) {
+    return GEMM_ERR_OUT_OF_MEMORY;
+  } catch (...) {
+    return GEMM_ERR_HIP;
+  }
+}
 
 std::mutex g_mu;
 std::unordered_set<const tgemm_handle*>& live() {
@@ -222,6 +271,15 @@ struct Stored {
 };
 int64_t packed_ld(int64_t cols) { return cdiv(cols, kRepackAlign) * kRepackAlign; }
 int64_t packed_bytes(const Stored& x) { return x.rows * packed_ld(x.cols) * 2; }
+// Workspace of split-K over an M x N part: S dense fp32 slices.
+size_t split_bytes(int64_t splits, int64_t M, int64_t N) { return (size_t)splits * (size_t)M * (size_t)N * sizeof(float); }
+// Operand copies (bit 0 A, bit 1 B): A's copy first, B's at the next 256-byte boundary.
+size_t pack_offset_b(int repack, const Stored& a) {
+  return (repack & 1) ? ((size_t)packed_bytes(a) + 255) / 256 * 256 : 0;
+}
+size_t pack_bytes(int repack, const Stored& a, const Stored& b) {
+  return pack_offset_b(repack, a) + ((repack & 2) ? (size_t)packed_bytes(b) : 0);
+}
 // Rows that do not start on 128-byte (cache line) boundaries: every 128-byte K-segment
 // of a K-contiguous row then spans two lines (a 512-byte segment of an M/N-contiguous
 // row five instead of four).
@@ -445,77 +503,89 @@ gemm_status_t gemm_check_args(int64_t M, int64_t N, int64_t K, const void* A, in
 gemm_status_t gemm_create(gemm_handle_t* out) {
   if (out == nullptr) return GEMM_ERR_INVALID_ARG;
   *out = nullptr;
-  int count = 0;
-  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
-    (void)hipGetLastError();
-    return GEMM_ERR_NO_DEVICE;
-  }
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_HIP;
-  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_ERR_ARCH;
-  tgemm_handle* h = new (std::nothrow) tgemm_handle;
-  if (h == nullptr) return GEMM_ERR_OUT_OF_MEMORY;
-  h->device = dev;
-  h->cus = prop.multiProcessorCount;
-  h->tm = h->tn = h->tk = 0;
-  h->splits = 0;
-  h->repack = 0;
-  h->ws = nullptr;
-  h->ws_bytes = 0;
-  h->pack = nullptr;
-  h->pack_bytes = 0;
-  {
-    std::lock_guard<std::mutex> g(g_mu);
-    live().insert(h);
-  }
-  *out = h;
-  return GEMM_OK;
+  return guarded([&]() -> gemm_status_t {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+      (void)hipGetLastError();
+      return GEMM_ERR_NO_DEVICE;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_ERR_ARCH;
+    std::unique_ptr<tgemm_handle> h(new tgemm_handle);
+    h->device = dev;
+    h->cus = prop.multiProcessorCount;
+    h->tm = h->tn = h->tk = 0;
+    h->splits = 0;
+    h->repack = 0;
+    h->ws[0] = h->ws[1] = nullptr;
+    h->ws_bytes[0] = h->ws_bytes[1] = 0;
+    {
+      std::lock_guard<std::mutex> g(g_mu);
+      live().insert(h.get());
+    }
+    *out = h.release();
+    return GEMM_OK;
+  });
 }
 
 gemm_status_t gemm_destroy(gemm_handle_t h) {
-  {
-    std::lock_guard<std::mutex> g(g_mu);
-    if (h == nullptr || live().erase(h) == 0) return GEMM_ERR_INVALID_ARG;
-  }
-  gemm_status_t st = GEMM_OK;
-  if (h->ws != nullptr && hipFree(h->ws) != hipSuccess) st = GEMM_ERR_HIP;  // waits for work using it
-  if (h->pack != nullptr && hipFree(h->pack) != hipSuccess) st = GEMM_ERR_HIP;
-  delete h;
-  return st;
+  return guarded([&]() -> gemm_status_t {
+    {
+      std::lock_guard<std::mutex> g(g_mu);
+      if (h == nullptr || live().erase(h) == 0) return GEMM_ERR_INVALID_ARG;
+    }
+    gemm_status_t st = GEMM_OK;
+    // hipFree waits for work still using a buffer
+    for (void* p : {h->ws[0], h->ws[1]})
+      if (p != nullptr && hipFree(p) != hipSuccess) st = GEMM_ERR_HIP;
+    for (void* p : h->retired)
+      if (hipFree(p) != hipSuccess) st = GEMM_ERR_HIP;
+    delete h;
+    return st;
+  });
 }
 
 gemm_status_t gemm_set_tile(gemm_handle_t h, int32_t tm, int32_t tn, int32_t tk) {
-  if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
-  const bool all_zero = tm == 0 && tn == 0 && tk == 0;
-  if (!all_zero && (tm <= 0 || tn <= 0 || tk <= 0)) return GEMM_ERR_INVALID_ARG;
-  h->tm = tm;
-  h->tn = tn;
-  h->tk = tk;
-  return GEMM_OK;
+  return guarded([&]() -> gemm_status_t {
+    if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
+    const bool all_zero = tm == 0 && tn == 0 && tk == 0;
+    if (!all_zero && (tm <= 0 || tn <= 0 || tk <= 0)) return GEMM_ERR_INVALID_ARG;
+    h->tm = tm;
+    h->tn = tn;
+    h->tk = tk;
+    return GEMM_OK;
+  });
 }
 
 gemm_status_t gemm_set_split_k(gemm_handle_t h, int32_t splits) {
-  if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
-  if (splits < 0 || splits > kMaxSplits) return GEMM_ERR_INVALID_ARG;
-  h->splits = splits;
-  return GEMM_OK;
+  return guarded([&]() -> gemm_status_t {
+    if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
+    if (splits < 0 || splits > kMaxSplits) return GEMM_ERR_INVALID_ARG;
+    h->splits = splits;
+    return GEMM_OK;
+  });
 }
 
 gemm_status_t gemm_set_repack(gemm_handle_t h, int32_t mode) {
-  if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
-  if (mode < -1 || mode > 1) return GEMM_ERR_INVALID_ARG;
-  h->repack = mode;
-  return GEMM_OK;
+  return guarded([&]() -> gemm_status_t {
+    if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
+    if (mode < -1 || mode > 1) return GEMM_ERR_INVALID_ARG;
+    h->repack = mode;
+    return GEMM_OK;
+  });
 }
 
 gemm_status_t gemm_plan_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K,
                            const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc,
                            gemm_dtype_t dtype, gemm_plan_t* out) {
-  if (out == nullptr) return GEMM_ERR_INVALID_ARG;
-  if (h != nullptr && !is_live(h)) return GEMM_ERR_INVALID_ARG;
-  return plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, out);
+  return guarded([&]() -> gemm_status_t {
+    if (out == nullptr) return GEMM_ERR_INVALID_ARG;
+    if (h != nullptr && !is_live(h)) return GEMM_ERR_INVALID_ARG;
+    return plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, out);
+  });
 }
 
 gemm_status_t gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -531,24 +601,14 @@ namespace {
 // Enqueue the MFMA kernels of plan p for an M x N part of C (rows of A and C already
 // offset by the caller) with the given K-slice count: one launch, or the slices'
 // partial tiles into the handle's workspace and the ordered reduction.
-gemm_status_t launch_mfma_part(tgemm_handle* h, const gemm_plan_t& p, int splits, bool ta, bool tb, int64_t M,
+gemm_status_t launch_mfma_part(WsSource& wsrc, const gemm_plan_t& p, int splits, bool ta, bool tb, int64_t M,
                                int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                                int64_t ldc, int dtype, hipStream_t s) {
+  void* ws = nullptr;
   if (splits > 1) {
-    const size_t need = (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
-    if (h->ws_bytes < need) {
-      if (h->ws != nullptr) {
-        if (hipFree(h->ws) != hipSuccess) return GEMM_ERR_HIP;
-        h->ws = nullptr;
-        h->ws_bytes = 0;
-      }
-      if (hipMalloc(&h->ws, need) != hipSuccess) {
-        (void)hipGetLastError();
-        h->ws = nullptr;
-        return GEMM_ERR_OUT_OF_MEMORY;
-      }
-      h->ws_bytes = need;
-    }
+    gemm_status_t st = GEMM_OK;
+    ws = wsrc.get(WS_SPLIT, split_bytes(splits, M, N), &st);
+    if (ws == nullptr) return st;
   }
   const int64_t grid = cdiv(M, p.tile_m) * cdiv(N, p.tile_n);
   tg::MacroArgs a;
@@ -577,21 +637,21 @@ gemm_status_t launch_mfma_part(tgemm_handle* h, const gemm_plan_t& p, int splits
   } else {
     // partial tiles (fp32, dense, ldc = N) into the workspace, then the ordered reduction
     tg::MacroArgs w = a;
-    w.C = h->ws;
+    w.C = ws;
     w.ldc = N;
-    w.c_vec = 1;  // hipMalloc'ed workspace: 256-byte aligned fp32
+    w.c_vec = 1;  // 256-byte aligned fp32 workspace
     e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k, p.stages), w, in_kind(dtype), 0, p.vector_loads != 0,
                          s, grid, splits, ta, tb);
     if (e == hipSuccess)
-      e = tg::launch_splitk_reduce((const float*)h->ws, splits, C, ldc, (int)M, (int)N, out_kind(dtype), s);
+      e = tg::launch_splitk_reduce((const float*)ws, splits, C, ldc, (int)M, (int)N, out_kind(dtype), s);
   }
   return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
 // Enqueue the kernels of plan p (arguments already checked).
-gemm_status_t launch_plan(tgemm_handle* h, const gemm_plan_t& p, bool ta, bool tb, int64_t M, int64_t N, int64_t K,
-                          const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int dtype,
-                          hipStream_t s) {
+gemm_status_t launch_plan(WsSource& wsrc, const gemm_plan_t& p, bool ta, bool tb, int64_t M, int64_t N,
+                          int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                          int dtype, hipStream_t s) {
   hipError_t e = hipSuccess;
   switch (p.kernel) {
     case 0: return GEMM_OK;
@@ -620,50 +680,39 @@ gemm_status_t launch_plan(tgemm_handle* h, const gemm_plan_t& p, bool ta, bool t
       if (p.kernel == 4 && p.repack != 0) {
         // copy the flagged operands into aligned rows of the handle's workspace first
         const Stored sa{ta ? K : M, ta ? M : K, lda, A, !ta}, sb{tb ? N : K, tb ? K : N, ldb, B, tb};
-        const size_t bytes_a = (p.repack & 1) ? (size_t)packed_bytes(sa) : 0;
-        const size_t bytes_b = (p.repack & 2) ? (size_t)packed_bytes(sb) : 0;
-        const size_t off_b = (bytes_a + 255) / 256 * 256, need = off_b + bytes_b;
-        if (h->pack_bytes < need) {
-          if (h->pack != nullptr) {
-            if (hipFree(h->pack) != hipSuccess) return GEMM_ERR_HIP;
-            h->pack = nullptr;
-            h->pack_bytes = 0;
-          }
-          if (hipMalloc(&h->pack, need) != hipSuccess) {
-            (void)hipGetLastError();
-            h->pack = nullptr;
-            return GEMM_ERR_OUT_OF_MEMORY;
-          }
-          h->pack_bytes = need;
-        }
+        const size_t off_b = pack_offset_b(p.repack, sa);
+        gemm_status_t st = GEMM_OK;
+        void* pack = wsrc.get(WS_PACK, pack_bytes(p.repack, sa, sb), &st);
+        if (pack == nullptr) return st;
         gemm_plan_t q = p;
         q.repack = 0;
         if (p.repack & 1) {
-          uint16_t* dst = (uint16_t*)h->pack;
+          uint16_t* dst = (uint16_t*)pack;
           if (tg::launch_repack((const uint16_t*)A, lda, dst, packed_ld(sa.cols), sa.rows, sa.cols, s) != hipSuccess)
             return GEMM_ERR_HIP;
           A = dst;
           lda = packed_ld(sa.cols);
         }
         if (p.repack & 2) {
-          uint16_t* dst = (uint16_t*)((char*)h->pack + off_b);
+          uint16_t* dst = (uint16_t*)((char*)pack + off_b);
           if (tg::launch_repack((const uint16_t*)B, ldb, dst, packed_ld(sb.cols), sb.rows, sb.cols, s) != hipSuccess)
             return GEMM_ERR_HIP;
           B = dst;
           ldb = packed_ld(sb.cols);
         }
-        return launch_plan(h, q, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, dtype, s);
+        return launch_plan(wsrc, q, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, dtype, s);
       }
       if (p.kernel == 4 && p.tail_split_k > 1 && p.tail_m0 > 0 && p.tail_m0 < M) {
         // the full rounds of tiles, then the tail rows with their K ranges split
         const int64_t m0 = p.tail_m0;
-        gemm_status_t st = launch_mfma_part(h, p, 1, ta, tb, m0, N, K, A, lda, B, ldb, C, ldc, dtype, s);
+        gemm_status_t st = launch_mfma_part(wsrc, p, 1, ta, tb, m0, N, K, A, lda, B, ldb, C, ldc, dtype, s);
         if (st != GEMM_OK) return st;
         const void* A2 = (const char*)A + (ta ? m0 : m0 * lda) * 2;
         void* C2 = (char*)C + m0 * ldc * out_bytes(dtype);
-        return launch_mfma_part(h, p, p.tail_split_k, ta, tb, M - m0, N, K, A2, lda, B, ldb, C2, ldc, dtype, s);
+        return launch_mfma_part(wsrc, p, p.tail_split_k, ta, tb, M - m0, N, K, A2, lda, B, ldb, C2, ldc, dtype, s);
       }
-      return launch_mfma_part(h, p, p.split_k > 1 ? p.split_k : 1, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, dtype, s);
+      return launch_mfma_part(wsrc, p, p.split_k > 1 ? p.split_k : 1, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, dtype,
+                              s);
     }
   }
   return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
@@ -676,145 +725,155 @@ extern "C" {
 gemm_status_t gemm_run_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K,
                           const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                           gemm_dtype_t dtype, void* stream) {
-  if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
-  gemm_plan_t p;
-  gemm_status_t st = plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &p);
-  if (st != GEMM_OK) return st;
-  const bool ta = op_a == GEMM_OP_T, tb = op_b == GEMM_OP_T;
-  static const bool log = std::getenv("TGEMM_LOG") != nullptr;
-  if (log)
-    std::fprintf(stderr,
-                 "tgemm: op=%c%c M=%lld N=%lld K=%lld dtype=%d kernel=%d tile=%dx%dx%d threads=%d vec=%d grid=%lld "
-                 "split_k=%d stages=%d\n",
-                 ta ? 'T' : 'N', tb ? 'T' : 'N', (long long)M, (long long)N, (long long)K, (int)dtype, p.kernel,
-                 p.tile_m, p.tile_n, p.tile_k, p.threads, p.vector_loads, (long long)p.grid, p.split_k, p.stages);
-  return launch_plan(h, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, (hipStream_t)stream);
+  return guarded([&]() -> gemm_status_t {
+    if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
+    gemm_plan_t p;
+    gemm_status_t st = plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &p);
+    if (st != GEMM_OK) return st;
+    const bool ta = op_a == GEMM_OP_T, tb = op_b == GEMM_OP_T;
+    static const bool log = std::getenv("TGEMM_LOG") != nullptr;
+    if (log)
+      std::fprintf(stderr,
+                   "tgemm: op=%c%c M=%lld N=%lld K=%lld dtype=%d kernel=%d tile=%dx%dx%d threads=%d vec=%d grid=%lld "
+                   "split_k=%d stages=%d\n",
+                   ta ? 'T' : 'N', tb ? 'T' : 'N', (long long)M, (long long)N, (long long)K, (int)dtype, p.kernel,
+                   p.tile_m, p.tile_n, p.tile_k, p.threads, p.vector_loads, (long long)p.grid, p.split_k, p.stages);
+    HandleWs wsrc(h);
+    return launch_plan(wsrc, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, (hipStream_t)stream);
+  });
 }
 
 gemm_status_t gemm_tune(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K,
                         const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                         gemm_dtype_t dtype, void* stream, int32_t iters, gemm_plan_t* best) {
-  if (!is_live(h) || best == nullptr || iters < 1 || iters > kMaxTuneIters) return GEMM_ERR_INVALID_ARG;
-  gemm_plan_t base;
-  gemm_status_t st = plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &base);
-  if (st != GEMM_OK) return st;
-  // Nothing to choose: forced settings, the integer path, empty products.
-  if (h->tm != 0 || h->splits != 0 || (base.kernel != 3 && base.kernel != 4)) {
-    *best = base;
-    return GEMM_OK;
-  }
-  const tune_key key{M, N, K, (int)op_a, (int)op_b, (int)dtype, base.vector_loads};
-  h->tuned.erase(key);
-  st = plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &base);  // the automatic plan
-  if (st != GEMM_OK) return st;
-  const bool ta = op_a == GEMM_OP_T, tb = op_b == GEMM_OP_T;
-  const bool vec = base.vector_loads != 0;
-
-  // Candidates: the automatic plan when it has a split-K tail, every 2-stage macro
-  // tile with K-slice counts up to 32 (each slice at least 2 K-tiles), the 4-stage
-  // twins where they apply, and the one-wave 16x16x32 tile for small outputs.
-  std::vector<tune_choice> cand;
-  auto add = [&](const tune_choice& c) {
-    for (const tune_choice& d : cand)
-      if (d.kernel == c.kernel && d.tm == c.tm && d.tn == c.tn && d.split_k == c.split_k && d.stages == c.stages &&
-          d.tail_split_k == c.tail_split_k && d.tail_m0 == c.tail_m0)
-        return;
-    cand.push_back(c);
-  };
-  if (base.kernel == 4 && base.tail_split_k > 1)
-    add(tune_choice{4, base.tile_m, base.tile_n, base.tile_k, 1, base.stages, base.tail_split_k, base.tail_m0});
-  const int shapes[] = {0, 1, 2, 3};
-  const int split_try[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
-  for (int si : shapes) {
-    const tg::MacroShape& m = tg::kMacroShapes[si];
-    if (vector_ok(M, N, K, A, lda, B, ldb, m.bm, m.bn, m.bk, ta, tb, true) != vec) continue;  // same loader as the plan
-    const int64_t grid = cdiv(M, m.bm) * cdiv(N, m.bn), nk = cdiv(K, m.bk);
-    for (int sk : split_try) {
-      if (sk > 1 && (nk / sk < 2 || grid * sk > kTuneMaxWorkgroups)) continue;
-      const int eff = sk > 1 ? (int)cdiv(nk, cdiv(nk, sk)) : 1;
-      add(tune_choice{4, m.bm, m.bn, m.bk, eff, 2});
-      if (vec && find_macro(m.bm, m.bn, m.bk, 4) >= 0 && cdiv(nk, eff) >= 4) add(tune_choice{4, m.bm, m.bn, m.bk, eff, 4});
+  return guarded([&]() -> gemm_status_t {
+    if (!is_live(h) || best == nullptr || iters < 1 || iters > kMaxTuneIters) return GEMM_ERR_INVALID_ARG;
+    gemm_plan_t base;
+    gemm_status_t st = plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &base);
+    if (st != GEMM_OK) return st;
+    // Nothing to choose: forced settings, the integer path, empty products.
+    if (h->tm != 0 || h->splits != 0 || (base.kernel != 3 && base.kernel != 4)) {
+      *best = base;
+      return GEMM_OK;
     }
-  }
-  // the 16x16x32 tile, where its (strict) loader choice is the plan's
-  if (M * N <= kTuneSmallTileMaxOutputs && vector_ok(M, N, K, A, lda, B, ldb, 16, 16, 32, ta, tb, false) == vec)
-    add(tune_choice{3, 16, 16, 32, 1, 2});
+    const tune_key key{M, N, K, (int)op_a, (int)op_b, (int)dtype, base.vector_loads};
+    h->tuned.erase(key);
+    st = plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &base);  // the automatic plan
+    if (st != GEMM_OK) return st;
+    const bool ta = op_a == GEMM_OP_T, tb = op_b == GEMM_OP_T;
+    const bool vec = base.vector_loads != 0;
 
-  hipStream_t s = (hipStream_t)stream;
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
-    if (e0) (void)hipEventDestroy(e0);
-    return GEMM_ERR_HIP;
-  }
-  float best_ms = 0.0f;
-  int best_i = -1;
-  for (size_t i = 0; i < cand.size() && st == GEMM_OK; ++i) {
+    // Candidates: the automatic plan when it has a split-K tail, every 2-stage macro
+    // tile with K-slice counts up to 32 (each slice at least 2 K-tiles), the 4-stage
+    // twins where they apply, and the one-wave 16x16x32 tile for small outputs.
+    std::vector<tune_choice> cand;
+    auto add = [&](const tune_choice& c) {
+      for (const tune_choice& d : cand)
+        if (d.kernel == c.kernel && d.tm == c.tm && d.tn == c.tn && d.split_k == c.split_k && d.stages == c.stages &&
+            d.tail_split_k == c.tail_split_k && d.tail_m0 == c.tail_m0)
+          return;
+      cand.push_back(c);
+    };
+    if (base.kernel == 4 && base.tail_split_k > 1)
+      add(tune_choice{4, base.tile_m, base.tile_n, base.tile_k, 1, base.stages, base.tail_split_k, base.tail_m0});
+    const int shapes[] = {0, 1, 2, 3};
+    const int split_try[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32};
+    for (int si : shapes) {
+      const tg::MacroShape& m = tg::kMacroShapes[si];
+      if (vector_ok(M, N, K, A, lda, B, ldb, m.bm, m.bn, m.bk, ta, tb, true) != vec) continue;  // same loader as the plan
+      const int64_t grid = cdiv(M, m.bm) * cdiv(N, m.bn), nk = cdiv(K, m.bk);
+      for (int sk : split_try) {
+        if (sk > 1 && (nk / sk < 2 || grid * sk > kTuneMaxWorkgroups)) continue;
+        const int eff = sk > 1 ? (int)cdiv(nk, cdiv(nk, sk)) : 1;
+        add(tune_choice{4, m.bm, m.bn, m.bk, eff, 2});
+        if (vec && find_macro(m.bm, m.bn, m.bk, 4) >= 0 && cdiv(nk, eff) >= 4) add(tune_choice{4, m.bm, m.bn, m.bk, eff, 4});
+      }
+    }
+    // the 16x16x32 tile, where its (strict) loader choice is the plan's
+    if (M * N <= kTuneSmallTileMaxOutputs && vector_ok(M, N, K, A, lda, B, ldb, 16, 16, 32, ta, tb, false) == vec)
+      add(tune_choice{3, 16, 16, 32, 1, 2});
+
+    hipStream_t s = (hipStream_t)stream;
+    HandleWs wsrc(h);
+    struct Events {  // destroyed on every way out, an exception included
+      hipEvent_t e0 = nullptr, e1 = nullptr;
+      ~Events() {
+        if (e0) (void)hipEventDestroy(e0);
+        if (e1) (void)hipEventDestroy(e1);
+      }
+    } ev;
+    if (hipEventCreate(&ev.e0) != hipSuccess || hipEventCreate(&ev.e1) != hipSuccess) return GEMM_ERR_HIP;
+    hipEvent_t e0 = ev.e0, e1 = ev.e1;
+    float best_ms = 0.0f;
+    int best_i = -1;
+    for (size_t i = 0; i < cand.size() && st == GEMM_OK; ++i) {
+      gemm_plan_t p = base;
+      apply_choice(cand[i], M, N, K, &p);
+      st = launch_plan(wsrc, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, s);  // warm-up (and workspace)
+      if (st != GEMM_OK) break;
+      if (hipEventRecord(e0, s) != hipSuccess) st = GEMM_ERR_HIP;
+      for (int r = 0; r < iters && st == GEMM_OK; ++r)
+        st = launch_plan(wsrc, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, s);
+      float ms = 0.0f;
+      if (st == GEMM_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                            hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+        st = GEMM_ERR_HIP;
+      if (st == GEMM_OK && (best_i < 0 || ms < best_ms)) {
+        best_ms = ms;
+        best_i = (int)i;
+      }
+    }
+    if (st != GEMM_OK) return st;
+    h->tuned[key] = cand[best_i];
     gemm_plan_t p = base;
-    apply_choice(cand[i], M, N, K, &p);
-    st = launch_plan(h, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, s);  // warm-up (and workspace)
-    if (st != GEMM_OK) break;
-    if (hipEventRecord(e0, s) != hipSuccess) st = GEMM_ERR_HIP;
-    for (int r = 0; r < iters && st == GEMM_OK; ++r)
-      st = launch_plan(h, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, s);
-    float ms = 0.0f;
-    if (st == GEMM_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
-                          hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
-      st = GEMM_ERR_HIP;
-    if (st == GEMM_OK && (best_i < 0 || ms < best_ms)) {
-      best_ms = ms;
-      best_i = (int)i;
-    }
-  }
-  (void)hipEventDestroy(e0);
-  (void)hipEventDestroy(e1);
-  if (st != GEMM_OK) return st;
-  h->tuned[key] = cand[best_i];
-  gemm_plan_t p = base;
-  apply_choice(cand[best_i], M, N, K, &p);
-  *best = p;
-  return GEMM_OK;
+    apply_choice(cand[best_i], M, N, K, &p);
+    *best = p;
+    return GEMM_OK;
+  });
 }
 
 gemm_status_t gemm_model(const gemm_plan_t* plan, int64_t M, int64_t N, int64_t K, gemm_dtype_t dtype,
                          gemm_model_t* out) {
-  if (plan == nullptr || out == nullptr) return GEMM_ERR_INVALID_ARG;
-  const int d = (int)dtype;
-  if (d < GEMM_I32_I32 || d > GEMM_F16_F16) return GEMM_ERR_UNSUPPORTED_DTYPE;
-  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
-  const gemm_plan_t& p = *plan;
-  if (p.kernel < 0 || p.kernel > 4) return GEMM_ERR_INVALID_ARG;
-  gemm_model_t m;
-  std::memset(&m, 0, sizeof(m));
-  const double s_in = d == GEMM_I32_I32 ? 4.0 : 2.0, s_out = (double)out_bytes(d);
-  const double dM = (double)M, dN = (double)N, dK = (double)K;
-  m.flops = 2.0 * dM * dN * dK;
-  m.compulsory_bytes = s_in * (dM * dK + dK * dN) + s_out * dM * dN;
-  if (M > 0 && N > 0) m.bytes_c = s_out * dM * dN;  // the zero fill (K = 0) writes C too
-  if (p.kernel >= 2) {
-    if (p.tile_m <= 0 || p.tile_n <= 0 || p.tile_k <= 0 || p.split_k < 1) return GEMM_ERR_INVALID_ARG;
-    const int64_t tm = cdiv(M, p.tile_m), tn = cdiv(N, p.tile_n), nk = cdiv(K, p.tile_k);
-    m.tiles = tm * tn;
-    m.k_steps = nk;
-    m.bytes_a = s_in * dM * dK * (double)tn;
-    m.bytes_b = s_in * dK * dN * (double)tm;
-    m.footprint_bytes = (int64_t)(s_in * (p.tile_m * p.tile_k + p.tile_k * p.tile_n)) + 4LL * p.tile_m * p.tile_n;
-    m.lds_bytes = p.lds_bytes;
-    const double tile_mn = (double)p.tile_m * p.tile_n * (double)m.tiles;
-    if (p.kernel == 2) {
-      m.executed_flops = 2.0 * tile_mn * dK;  // every thread of a tile runs the actual K range
-    } else {
-      // every tile runs its K-tiles (split into K-slices or not), the last one zero-padded
-      m.executed_flops = 2.0 * tile_mn * (double)(nk * p.tile_k);
-      if (p.kernel == 4 && p.tail_split_k > 1 && p.tail_m0 > 0 && p.tail_m0 < M)
-        m.bytes_workspace = 2.0 * 4.0 * (double)p.tail_split_k * (double)(M - p.tail_m0) * dN;
+  return guarded([&]() -> gemm_status_t {
+    if (plan == nullptr || out == nullptr) return GEMM_ERR_INVALID_ARG;
+    const int d = (int)dtype;
+    if (d < GEMM_I32_I32 || d > GEMM_F16_F16) return GEMM_ERR_UNSUPPORTED_DTYPE;
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+    const gemm_plan_t& p = *plan;
+    if (p.kernel < 0 || p.kernel > 4) return GEMM_ERR_INVALID_ARG;
+    gemm_model_t m;
+    std::memset(&m, 0, sizeof(m));
+    const double s_in = d == GEMM_I32_I32 ? 4.0 : 2.0, s_out = (double)out_bytes(d);
+    const double dM = (double)M, dN = (double)N, dK = (double)K;
+    m.flops = 2.0 * dM * dN * dK;
+    m.compulsory_bytes = s_in * (dM * dK + dK * dN) + s_out * dM * dN;
+    if (M > 0 && N > 0) m.bytes_c = s_out * dM * dN;  // the zero fill (K = 0) writes C too
+    if (p.kernel >= 2) {
+      if (p.tile_m <= 0 || p.tile_n <= 0 || p.tile_k <= 0 || p.split_k < 1) return GEMM_ERR_INVALID_ARG;
+      const int64_t tm = cdiv(M, p.tile_m), tn = cdiv(N, p.tile_n), nk = cdiv(K, p.tile_k);
+      m.tiles = tm * tn;
+      m.k_steps = nk;
+      m.bytes_a = s_in * dM * dK * (double)tn;
+      m.bytes_b = s_in * dK * dN * (double)tm;
+      m.footprint_bytes = (int64_t)(s_in * (p.tile_m * p.tile_k + p.tile_k * p.tile_n)) + 4LL * p.tile_m * p.tile_n;
+      m.lds_bytes = p.lds_bytes;
+      const double tile_mn = (double)p.tile_m * p.tile_n * (double)m.tiles;
+      if (p.kernel == 2) {
+        m.executed_flops = 2.0 * tile_mn * dK;  // every thread of a tile runs the actual K range
+      } else {
+        // every tile runs its K-tiles (split into K-slices or not), the last one zero-padded
+        m.executed_flops = 2.0 * tile_mn * (double)(nk * p.tile_k);
+        if (p.kernel == 4 && p.tail_split_k > 1 && p.tail_m0 > 0 && p.tail_m0 < M)
+          m.bytes_workspace = 2.0 * 4.0 * (double)p.tail_split_k * (double)(M - p.tail_m0) * dN;
+      }
+      if (p.split_k > 1) m.bytes_workspace = 2.0 * 4.0 * (double)p.split_k * dM * dN;
+      // operand copies: each flagged operand read and written once
+      if (p.kernel == 4 && (p.repack & 1)) m.bytes_workspace += 2.0 * s_in * dM * dK;
+      if (p.kernel == 4 && (p.repack & 2)) m.bytes_workspace += 2.0 * s_in * dK * dN;
     }
-    if (p.split_k > 1) m.bytes_workspace = 2.0 * 4.0 * (double)p.split_k * dM * dN;
-    // operand copies: each flagged operand read and written once
-    if (p.kernel == 4 && (p.repack & 1)) m.bytes_workspace += 2.0 * s_in * dM * dK;
-    if (p.kernel == 4 && (p.repack & 2)) m.bytes_workspace += 2.0 * s_in * dK * dN;
-  }
-  *out = m;
-  return GEMM_OK;
+    *out = m;
+    return GEMM_OK;
+  });
 }
 
 gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,

@@ -11,7 +11,8 @@ only maps tensors to the C entry point's arguments:
   column-major view, e.g. ``w.t()`` of a row-major ``w``, is passed as its
   row-major transpose (``GEMM_OP_T``), so transposed operands cost no copy;
 * the result is allocated with ``torch.empty`` (device memory only) unless
-  ``out`` is given; the work is enqueued on the current stream of ``a``'s device.
+  ``out`` is given; the work is enqueued on the current stream of ``a``'s device,
+  through a library handle of that host thread, device and stream.
 
 Other strides raise ``ValueError``: nothing is copied or converted here.
 """
@@ -21,19 +22,24 @@ import threading
 
 from . import tgemm
 
-_local = threading.local()  # one handle per host thread and device (a handle is single-threaded)
+# One handle per host thread, device and stream. A handle is single-threaded, and the
+# calls that use its workspaces (split-K partial tiles, operand copies) must be ordered:
+# calls on one stream are, and calls on different streams (a graph capture runs on a
+# stream of its own) get different handles, so they never share a workspace.
+_local = threading.local()
 
 
-def _handle(device_index: int):
+def _handle(device_index: int, stream: int):
     import torch
 
     hs = getattr(_local, "handles", None)
     if hs is None:
         hs = _local.handles = {}
-    g = hs.get(device_index)
+    key = (device_index, stream)
+    g = hs.get(key)
     if g is None:
         with torch.cuda.device(device_index):
-            g = hs[device_index] = tgemm.Gemm()
+            g = hs[key] = tgemm.Gemm()
     return g.h
 
 
@@ -104,9 +110,9 @@ def matmul(a, b, *, out_dtype=None, out=None):
     c = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=a.device)
     ldc = c.stride(0) if M > 1 else max(N, 1)
     dev = a.device.index if a.device.index is not None else torch.cuda.current_device()
-    h = _handle(dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream().cuda_stream
+        h = _handle(dev, stream)
         st = tgemm.gemm_run_op(h, op_a, op_b, M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, c.data_ptr(), ldc,
                                code, stream)
     tgemm.check(st, "gemm_run_op")
