@@ -68,7 +68,8 @@ typedef enum TGEMM_ENUM_BASE {
   GEMM_ERR_ARCH = 4,              /* current device is not gfx950 */
   GEMM_ERR_HIP = 5,               /* a HIP runtime call or kernel launch failed */
   GEMM_ERR_OUT_OF_MEMORY = 6,     /* a host allocation, or a device workspace allocation, failed */
-  GEMM_ERR_UNSUPPORTED_TILE = 7   /* gemm_set_tile asked for a tile no kernel has, for this dtype */
+  GEMM_ERR_UNSUPPORTED_TILE = 7,  /* gemm_set_tile asked for a tile no kernel has, for this dtype */
+  GEMM_ERR_SCRATCH_TOO_SMALL = 8  /* gemm_run_op_noalloc: the split-K partial tiles exceed its scratch */
 } gemm_status_t;
 
 /* Input/accumulator/output formats (int32). */
@@ -189,6 +190,25 @@ gemm_status_t gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, const v
 gemm_status_t gemm_run_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N, int64_t K,
                           const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                           gemm_dtype_t dtype, void* stream);
+
+/* gemm_run_op for callers that cannot allocate memory (code under HIP graph
+ * capture, serving loops that must not allocate, harnesses that forbid it): the same
+ * arguments, errors and results, and no allocation of any kind -- no hipMalloc,
+ * hipFree or allocating library call, host or device. The split-K partial tiles go
+ * to a fixed scratch array of 32 MiB in device memory (one per GPU, set up by
+ * gemm_create on that GPU and held until the process ends) instead of the handle's
+ * workspace: a call whose plan splits K into S slices needs S * M * N * 4 bytes of it
+ * (gemm_plan reports split_k), and one that needs more returns
+ * GEMM_ERR_SCRATCH_TOO_SMALL before anything is enqueued. Operands are never copied
+ * into aligned rows here (the results do not depend on it), and a split-K tail runs
+ * only if its partial tiles fit; otherwise the plan is gemm_run_op's. The scratch
+ * array holds the last call's partial tiles; nothing in it needs to start at zero.
+ * Every call on one GPU shares that GPU's array, so calls that may overlap on one
+ * GPU (different streams, different handles, different host threads) race and must
+ * be ordered by the caller. h must have been created on the device the call runs on. */
+gemm_status_t gemm_run_op_noalloc(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N,
+                                  int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                                  int64_t ldc, gemm_dtype_t dtype, void* stream);
 
 /* Choose the fastest plan for one call's shape by measurement (the pages' Helion
  * page: the compiler tunes the tile size automatically). Runs every candidate --

@@ -1,10 +1,10 @@
 // Allocation failures at the C interface, without a GPU.
 //
 // The executable defines its own global operator new / delete (counting live blocks
-// and throwing std::bad_alloc once an armed countdown runs out) and the three device
-// queries gemm_create makes (one visible gfx950 device). Linked with -rdynamic, these
-// definitions take the place of libstdc++'s and the HIP runtime's for every caller in
-// the process, libtgemm.so included. Each entry point that allocates host memory must
+// and throwing std::bad_alloc once an armed countdown runs out) and the device calls
+// gemm_create makes (one visible gfx950 device, the address of the scratch array).
+// Linked with -rdynamic, these definitions take the place of libstdc++'s and the HIP
+// runtime's for every caller in the process, libtgemm.so included. Each entry point that allocates host memory must
 // then return GEMM_ERR_OUT_OF_MEMORY, with no exception escaping and nothing leaked.
 #include <hip/hip_runtime_api.h>
 
@@ -58,6 +58,12 @@ extern "C" hipError_t hipGetDevicePropertiesR0600(hipDeviceProp_tR0600* prop, in
   std::memset(prop, 0, sizeof(*prop));
   std::strcpy(prop->gcnArchName, "gfx950:sramecc+:xnack-");
   prop->multiProcessorCount = 256;
+  return hipSuccess;
+}
+
+// The device address of the library's scratch array (resolved by gemm_create).
+extern "C" hipError_t hipGetSymbolAddress(void** ptr, const void*) {
+  *ptr = reinterpret_cast<void*>(static_cast<uintptr_t>(0x200000));
   return hipSuccess;
 }
 

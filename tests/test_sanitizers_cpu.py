@@ -3,7 +3,9 @@
 - The oracle (oracle/oracle.c) with gcc's sanitizers, driven by tests/c_abi/oracle_client.c:
   every entry point on empty, ragged and padded cases, every kind, several thread counts.
 - The library's host side (csrc/api.hip: argument checks, planning, counts, status strings)
-  recompiled host-only with the sanitizers and linked with the already built kernel objects;
+  recompiled with the sanitizers on its host code only (its device part, the scratch array
+  of the allocation-free entry point, is built as usual) and linked with the already built
+  kernel objects;
   the C client tests/c_abi/abi_client.c, built with the same compiler's sanitizers, runs its
   host checks and a sweep of 13,005 plans over shapes, paddings, odd addresses, operand forms
   and dtypes. No device code is instrumented and no GPU is used.
@@ -51,7 +53,7 @@ def test_host_library_under_sanitizers(tmp_path):
     if not objs or not os.path.exists(HIPCC) or not os.path.exists(CLANG):
         pytest.skip("kernel objects or the ROCm compilers are missing (run the build first)")
     api = str(tmp_path / "api_san.o")
-    run([HIPCC, "--offload-arch=gfx950", "--cuda-host-only", "-O1", "-g", "-std=c++17", "-fPIC",
+    run([HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC",
          "-fno-omit-frame-pointer", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, *HOST_SAN, "-c",
          os.path.join(CSRC, "api.hip"), "-o", api])
     lib = str(tmp_path / "libtgemm_san.so")

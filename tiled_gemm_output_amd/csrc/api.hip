@@ -38,6 +38,11 @@ struct tune_choice {
   int tail_split_k = 0, tail_m0 = 0;  // a split-K tail after the full rounds (the automatic plan's)
 };
 
+// Scratch memory of gemm_run_op_noalloc: one array on every GPU the library runs on,
+// held until the process ends. Only the split-K partial tiles use it (S x M x N fp32).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 // Device memory a call's kernels may use besides A, B and C: the fp32 partial tiles
 // of split-K (WS_SPLIT) and operand copies into aligned rows (WS_PACK).
 enum WsKind { WS_SPLIT = 0, WS_PACK = 1 };
@@ -85,6 +90,46 @@ struct HandleWs final : WsSource {
     h->ws[kind] = p;
     h->ws_bytes[kind] = bytes;
     return p;
+  }
+};
+
+// Device address of each GPU's scratch array, resolved once per device by gemm_create
+// with that device current (in host code `scratch` names a host-side stand-in, not
+// device memory).
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+gemm_status_t resolve_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return GEMM_OK;  // gemm_run_op_noalloc refuses such devices
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_ptr[dev] != nullptr) return GEMM_OK;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+    (void)hipGetLastError();
+    return GEMM_ERR_HIP;
+  }
+  g_scratch_ptr[dev] = p;
+  return GEMM_OK;
+}
+
+void* scratch_of(int dev) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  return g_scratch_ptr[dev];
+}
+
+// The scratch array as a workspace: split-K partial tiles of up to kScratchBytes;
+// nothing is ever allocated.
+struct ScratchWs final : WsSource {
+  void* base;
+  explicit ScratchWs(void* b) : base(b) {}
+  void* get(WsKind kind, size_t bytes, gemm_status_t* st) override {
+    if (kind != WS_SPLIT || bytes > kScratchBytes) {
+      *st = GEMM_ERR_SCRATCH_TOO_SMALL;
+      return nullptr;
+    }
+    return base;
   }
 };
 
@@ -472,6 +517,8 @@ const char* gemm_status_string(gemm_status_t s) {
     case GEMM_ERR_HIP: return "GEMM_ERR_HIP: HIP runtime or launch failure";
     case GEMM_ERR_OUT_OF_MEMORY: return "GEMM_ERR_OUT_OF_MEMORY: allocation of the handle or workspace failed";
     case GEMM_ERR_UNSUPPORTED_TILE: return "GEMM_ERR_UNSUPPORTED_TILE: no kernel has this tile for this dtype";
+    case GEMM_ERR_SCRATCH_TOO_SMALL:
+      return "GEMM_ERR_SCRATCH_TOO_SMALL: the call's split-K partial tiles need more than the 32 MiB scratch array";
   }
   return "unknown status";
 }
@@ -514,6 +561,8 @@ gemm_status_t gemm_create(gemm_handle_t* out) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_HIP;
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_ERR_ARCH;
+    const gemm_status_t sst = resolve_scratch(dev);
+    if (sst != GEMM_OK) return sst;
     std::unique_ptr<tgemm_handle> h(new tgemm_handle);
     h->device = dev;
     h->cus = prop.multiProcessorCount;
@@ -739,6 +788,33 @@ gemm_status_t gemm_run_op(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64
                    ta ? 'T' : 'N', tb ? 'T' : 'N', (long long)M, (long long)N, (long long)K, (int)dtype, p.kernel,
                    p.tile_m, p.tile_n, p.tile_k, p.threads, p.vector_loads, (long long)p.grid, p.split_k, p.stages);
     HandleWs wsrc(h);
+    return launch_plan(wsrc, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, (hipStream_t)stream);
+  });
+}
+
+gemm_status_t gemm_run_op_noalloc(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t M, int64_t N,
+                                  int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                                  int64_t ldc, gemm_dtype_t dtype, void* stream) {
+  return guarded([&]() -> gemm_status_t {
+    if (!is_live(h)) return GEMM_ERR_INVALID_ARG;
+    gemm_plan_t p;
+    gemm_status_t st = plan_impl(h, (int)op_a, (int)op_b, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, &p);
+    if (st != GEMM_OK) return st;
+    // No operand copies (they are as large as the operands; the kernels read unaligned
+    // rows as they are, with the same results), and a split-K tail only if its partial
+    // tiles fit. The split-K partial tiles of the plan itself must fit, or the call is
+    // refused before anything is enqueued.
+    p.repack = 0;
+    if (p.kernel == 4 && p.tail_split_k > 1 && split_bytes(p.tail_split_k, M - p.tail_m0, N) > kScratchBytes) {
+      p.tail_split_k = 0;
+      p.tail_m0 = 0;
+    }
+    if (p.kernel == 4 && p.split_k > 1 && split_bytes(p.split_k, M, N) > kScratchBytes)
+      return GEMM_ERR_SCRATCH_TOO_SMALL;
+    void* base = scratch_of(h->device);
+    if (base == nullptr) return GEMM_ERR_HIP;
+    ScratchWs wsrc(base);
+    const bool ta = op_a == GEMM_OP_T, tb = op_b == GEMM_OP_T;
     return launch_plan(wsrc, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, (hipStream_t)stream);
   });
 }

@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libtgemm.so")
 
 # gemm_status_t
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED_DTYPE, ERR_NO_DEVICE, ERR_ARCH, ERR_HIP, ERR_OUT_OF_MEMORY, ERR_UNSUPPORTED_TILE = range(8)
+(OK, ERR_INVALID_ARG, ERR_UNSUPPORTED_DTYPE, ERR_NO_DEVICE, ERR_ARCH, ERR_HIP, ERR_OUT_OF_MEMORY, ERR_UNSUPPORTED_TILE,
+ ERR_SCRATCH_TOO_SMALL) = range(9)
 # gemm_op_t
 OP_N, OP_T = 0, 1
 # gemm_dtype_t
@@ -28,7 +29,7 @@ IN_BYTES = {I32_I32: 4, F16_F32: 2, BF16_F32: 2, BF16_BF16: 2, F16_F16: 2}
 OUT_BYTES = {I32_I32: 4, F16_F32: 4, BF16_F32: 4, BF16_BF16: 2, F16_F16: 2}
 KERNEL_NAMES = {0: "none", 1: "zero_fill", 2: "int32_valu", 3: "mfma_16x16x32_one_wave", 4: "mfma_macro_tile"}
 
-EXPORTS = ["gemm_create", "gemm_run", "gemm_run_op", "gemm_tune", "gemm_destroy", "gemm_set_tile", "gemm_set_split_k",
+EXPORTS = ["gemm_create", "gemm_run", "gemm_run_op", "gemm_run_op_noalloc", "gemm_tune", "gemm_destroy", "gemm_set_tile", "gemm_set_split_k",
            "gemm_set_repack",
            "gemm_check_args", "gemm_check_args_op", "gemm_plan", "gemm_plan_op", "gemm_model", "gemm_status_string"]
 
@@ -80,6 +81,8 @@ def load(path: str = LIBRARY):
     lib.gemm_run.restype = i32
     lib.gemm_run_op.argtypes = [vp, i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, vp]
     lib.gemm_run_op.restype = i32
+    lib.gemm_run_op_noalloc.argtypes = [vp, i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, vp]
+    lib.gemm_run_op_noalloc.restype = i32
     lib.gemm_tune.argtypes = [vp, i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, vp, i32,
                               ctypes.POINTER(GemmPlan)]
     lib.gemm_tune.restype = i32
@@ -145,6 +148,10 @@ def gemm_run(h, M, N, K, A, lda, B, ldb, C, ldc, dtype, stream=None) -> int:
 
 def gemm_run_op(h, op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, dtype, stream=None) -> int:
     return load().gemm_run_op(h, int(op_a), int(op_b), M, N, K, A, lda, B, ldb, C, ldc, int(dtype), stream)
+
+
+def gemm_run_op_noalloc(h, op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, dtype, stream=None) -> int:
+    return load().gemm_run_op_noalloc(h, int(op_a), int(op_b), M, N, K, A, lda, B, ldb, C, ldc, int(dtype), stream)
 
 
 def gemm_tune(h, op_a, op_b, M, N, K, A, lda, B, ldb, C, ldc, dtype, stream=None, iters: int = 5) -> dict:
