@@ -35,15 +35,6 @@ extern const MacroShape kMacroShapes[kNumMacroShapes];
 // (K x M, row stride lda); tb: B is stored transposed (N x K, row stride ldb).
 hipError_t launch_macro(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
                         int splits, bool ta, bool tb);
-// one operand layout each (nn: neither operand transposed, nt: B, tn: A, tt: both)
-hipError_t launch_macro_nn(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
-                           int splits);
-hipError_t launch_macro_nt(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
-                           int splits);
-hipError_t launch_macro_tn(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
-                           int splits);
-hipError_t launch_macro_tt(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
-                           int splits);
 // C[0:M, 0:N] = sum over s < splits of ws[s][M][N] (dense fp32 partials, summed in slice order),
 // rounded to the output format (out: 0 = f32, 1 = bf16, 2 = f16).
 hipError_t launch_splitk_reduce(const float* ws, int splits, void* C, int64_t ldc, int M, int N, int out, hipStream_t s);

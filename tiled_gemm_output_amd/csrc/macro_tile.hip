@@ -1,8 +1,7 @@
 // macro_tile.hip -- launches of the macro-tile GEMM (the kernel is in
-// macro_tile_kernel.h): the table of tile shapes, the dispatch over operand
-// layouts, the untransposed layout's instantiations, and the split-K reduction.
-// The three transposed layouts are instantiated in macro_tile_{nt,tn,tt}.hip so
-// that they compile in parallel.
+// macro_tile_kernel.h): the table of tile shapes, the dispatch over operand layouts
+// and tiles, and the split-K reduction. The kernels themselves are instantiated in
+// macro_tile_inst_*.hip.
 #include "macro_tile_kernel.h"
 
 namespace tg {
@@ -80,17 +79,37 @@ const MacroShape kMacroShapes[kNumMacroShapes] = {
     {64, 64, 64, Cfg64x64s4::kThreads, Cfg64x64s4::kLds, Cfg64x64s4::NS},
 };
 
-hipError_t launch_macro_nn(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
-                           int splits) {
-  return launch_layout<false, false>(shape, a, in, out, vec, s, grid, splits);
+// The launchers live in macro_tile_inst_*.hip.
+#define TG_EXTERN(TA, TB, I, CFG)                                                                          \
+  extern template hipError_t launch_dtype<CFG, TA, TB>(const MacroArgs&, int, int, bool, hipStream_t, int64_t, \
+                                                       int);
+#define TG_EXTERN_NN(I, CFG) TG_EXTERN(false, false, I, CFG)
+#define TG_EXTERN_NT(I, CFG) TG_EXTERN(false, true, I, CFG)
+#define TG_EXTERN_TN(I, CFG) TG_EXTERN(true, false, I, CFG)
+#define TG_EXTERN_TT(I, CFG) TG_EXTERN(true, true, I, CFG)
+TG_MACRO_CONFIGS(TG_EXTERN_NN)
+TG_MACRO_CONFIGS(TG_EXTERN_NT)
+TG_MACRO_CONFIGS(TG_EXTERN_TN)
+TG_MACRO_CONFIGS(TG_EXTERN_TT)
+
+template <bool TA, bool TB>
+static hipError_t launch_layout(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
+                                int splits) {
+#define TG_CASE(I, CFG) \
+  case I: return launch_dtype<CFG, TA, TB>(a, in, out, vec, s, grid, splits);
+  switch (shape) {
+    TG_MACRO_CONFIGS(TG_CASE)
+    default: return hipErrorInvalidValue;
+  }
+#undef TG_CASE
 }
 
 hipError_t launch_macro(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
                         int splits, bool ta, bool tb) {
-  if (!ta && !tb) return launch_macro_nn(shape, a, in, out, vec, s, grid, splits);
-  if (!ta && tb) return launch_macro_nt(shape, a, in, out, vec, s, grid, splits);
-  if (ta && !tb) return launch_macro_tn(shape, a, in, out, vec, s, grid, splits);
-  return launch_macro_tt(shape, a, in, out, vec, s, grid, splits);
+  if (!ta && !tb) return launch_layout<false, false>(shape, a, in, out, vec, s, grid, splits);
+  if (!ta && tb) return launch_layout<false, true>(shape, a, in, out, vec, s, grid, splits);
+  if (ta && !tb) return launch_layout<true, false>(shape, a, in, out, vec, s, grid, splits);
+  return launch_layout<true, true>(shape, a, in, out, vec, s, grid, splits);
 }
 
 }  // namespace tg

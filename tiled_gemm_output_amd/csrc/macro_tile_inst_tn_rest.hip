@@ -1,0 +1,12 @@
+// macro_tile_inst_tn_rest.hip -- macro-tile GEMM kernels for C = A^T @ B (A supplied as K x M), the other tiles.
+#include "macro_tile_kernel.h"
+
+namespace tg {
+
+template hipError_t launch_dtype<Cfg256x128, true, false>(const MacroArgs&, int, int, bool, hipStream_t, int64_t, int);
+template hipError_t launch_dtype<Cfg128x128, true, false>(const MacroArgs&, int, int, bool, hipStream_t, int64_t, int);
+template hipError_t launch_dtype<Cfg64x64, true, false>(const MacroArgs&, int, int, bool, hipStream_t, int64_t, int);
+template hipError_t launch_dtype<Cfg128x128s4, true, false>(const MacroArgs&, int, int, bool, hipStream_t, int64_t, int);
+template hipError_t launch_dtype<Cfg64x64s4, true, false>(const MacroArgs&, int, int, bool, hipStream_t, int64_t, int);
+
+}  // namespace tg

@@ -739,9 +739,10 @@ static hipError_t launch_cfg(const MacroArgs& a, bool vec, hipStream_t stream, i
   return hipGetLastError();
 }
 
+// Instantiated explicitly, one compilation unit per operand layout and group of tiles
+// (macro_tile_inst_*.hip), so that they compile in parallel.
 template <class Cfg, bool TA, bool TB>
-static hipError_t launch_dtype(const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
-                               int splits) {
+hipError_t launch_dtype(const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid, int splits) {
   if (in == IN_BF16 && out == OUT_F32) return launch_cfg<Cfg, IN_BF16, OUT_F32, TA, TB>(a, vec, s, grid, splits);
   if (in == IN_BF16 && out == OUT_BF16) return launch_cfg<Cfg, IN_BF16, OUT_BF16, TA, TB>(a, vec, s, grid, splits);
   if (in == IN_F16 && out == OUT_F32) return launch_cfg<Cfg, IN_F16, OUT_F32, TA, TB>(a, vec, s, grid, splits);
@@ -749,18 +750,9 @@ static hipError_t launch_dtype(const MacroArgs& a, int in, int out, bool vec, hi
   return hipErrorInvalidValue;
 }
 
-template <bool TA, bool TB>
-static hipError_t launch_layout(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
-                                int splits) {
-  switch (shape) {
-    case 0: return launch_dtype<Cfg256x256w8, TA, TB>(a, in, out, vec, s, grid, splits);
-    case 1: return launch_dtype<Cfg256x128, TA, TB>(a, in, out, vec, s, grid, splits);
-    case 2: return launch_dtype<Cfg128x128, TA, TB>(a, in, out, vec, s, grid, splits);
-    case 3: return launch_dtype<Cfg64x64, TA, TB>(a, in, out, vec, s, grid, splits);
-    case 4: return launch_dtype<Cfg128x128s4, TA, TB>(a, in, out, vec, s, grid, splits);
-    case 5: return launch_dtype<Cfg64x64s4, TA, TB>(a, in, out, vec, s, grid, splits);
-    default: return hipErrorInvalidValue;
-  }
-}
+// The tile configurations, in the order of kMacroShapes (the shape index of launch_macro):
+// X(index, configuration).
+#define TG_MACRO_CONFIGS(X) \
+  X(0, Cfg256x256w8) X(1, Cfg256x128) X(2, Cfg128x128) X(3, Cfg64x64) X(4, Cfg128x128s4) X(5, Cfg64x64s4)
 
 }  // namespace tg

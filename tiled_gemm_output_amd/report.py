@@ -33,7 +33,8 @@ import sys
 
 from . import inputs, tgemm
 
-KERNELS = ("macro_tile_kernel", "small_tile_kernel", "i32_tile_kernel", "splitk_reduce_kernel", "zero_fill_kernel")
+KERNELS = ("macro_tile_kernel", "small_tile_kernel", "i32_tile_kernel", "splitk_reduce_kernel", "zero_fill_kernel",
+           "repack_rows_kernel")
 MFMA_MOP_FLOPS = 512  # flops per unit of SQ_INSTS_VALU_MFMA_MOPS_* (checked against the model in the report)
 
 
