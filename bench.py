@@ -94,10 +94,17 @@ def smi_gfx_clock_mhz():
         return None, None, None
 
 
+# The driver's metrics table, which amd-smi reads, is refreshed far less often than a launch
+# lasts (in process it changed once in the first 820 ms of load): readings in the first second
+# of the window may still show the clock from before the load, and are left out.
+CLOCK_SETTLE_S = 1.0
+
+
 def sample_clock_under_load(step, seconds: float):
-    """Keep launching ``step`` for ``seconds`` while sampling the gfx clock and socket power
-    with amd-smi in a second thread; returns the clock samples (MHz), the power samples
-    (W), both taken while the launches were running, and the reported maximum clock."""
+    """Keep launching ``step`` for CLOCK_SETTLE_S + ``seconds`` while sampling the gfx clock
+    and socket power with amd-smi in a second thread; returns the clock samples (MHz), the
+    power samples (W), both read after the first CLOCK_SETTLE_S seconds and while the
+    launches were running, and the reported maximum clock."""
     import threading
 
     import torch
@@ -107,26 +114,29 @@ def sample_clock_under_load(step, seconds: float):
 
     def sampler():
         while not stop.is_set():
+            t0 = time.perf_counter()
             mhz, mx, watts = smi_gfx_clock_mhz()
             if mhz is None:
                 return
-            samples.append((time.perf_counter(), mhz, watts))
+            samples.append((t0, time.perf_counter(), mhz, watts))
             top[0] = mx
 
     th = threading.Thread(target=sampler, daemon=True)
-    t_end = time.perf_counter() + seconds
+    t_keep = time.perf_counter() + CLOCK_SETTLE_S
+    t_end = t_keep + seconds
     for _ in range(20):
         step()
     th.start()
-    while time.perf_counter() < t_end or (th.is_alive() and not samples and time.perf_counter() < t_end + 10):
+    while time.perf_counter() < t_end or (th.is_alive() and not any(x[0] >= t_keep for x in samples)
+                                          and time.perf_counter() < t_end + 10):
         for _ in range(20):
             step()
         torch.cuda.synchronize()
     load_end = time.perf_counter()
     stop.set()
     th.join(timeout=20)
-    # only readings completed while the launches were still running
-    kept = [(mhz, watts) for t, mhz, watts in samples if t <= load_end]
+    # only readings taken after the settle time and completed while the launches were still running
+    kept = [(mhz, watts) for t0, t, mhz, watts in samples if t0 >= t_keep and t <= load_end]
     return [m for m, _ in kept], [w for _, w in kept if w is not None], top[0]
 
 
@@ -206,8 +216,8 @@ def main() -> int:
     # a 22 s target gives about 10-12 s of oracle work
     ap.add_argument("--cpu-seconds", type=float, default=22.0)
     ap.add_argument("--clock-window", type=float, default=2.0,
-                    help="seconds of further launches after the timed region, during which amd-smi samples "
-                         "the gfx clock (0: skip)")
+                    help="seconds of amd-smi clock readings kept while the launches continue after the timed "
+                         "region, after a first second whose readings are left out (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain device copy of 1 GiB (5 times): the known-size kernel whose "
@@ -374,7 +384,8 @@ def main() -> int:
             peak_now = PEAK_MFMA_16BIT_TFLOPS * med / top
             result["sclk"] = {
                 "source": "amd-smi metric -p -c (gfx clock, mean over XCDs; socket power), sampled while the same launches "
-                          "continue for %.1f s after the timed region" % args.clock_window,
+                          "continue for %.1f s after the timed region (readings of the first %.1f s left out)" % (
+                              CLOCK_SETTLE_S + args.clock_window, CLOCK_SETTLE_S),
                 "median_mhz": med, "min_mhz": float(np.min(samples)), "max_mhz": float(np.max(samples)),
                 "samples": len(samples), "max_clk_mhz": top,
                 "mfma_peak_at_median_tflops": peak_now,

@@ -10,7 +10,8 @@ counter group per run:
     rocprofv3 --pmc FETCH_SIZE -T -d D1 -o gemm -f csv -- python3 bench.py --workload W --no-cpu-baseline
     rocprofv3 --pmc WRITE_SIZE -T -d D2 -o gemm -f csv -- python3 bench.py --workload W --no-cpu-baseline
     rocprofv3 --pmc TCP_TCC_READ_REQ_sum -T -d D3 ...
-    rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 -T -d D4 ...
+    rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE \\
+        SQ_VALU_MFMA_BUSY_CYCLES -T -d D4 ...
     rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE ... -- python3 bench.py --copy-probe   (calibration)
 
     python -m tiled_gemm_output_amd.report --workload W --counters D1 D2 D3 D4 \\
@@ -36,6 +37,7 @@ from . import inputs, tgemm
 KERNELS = ("macro_tile_kernel", "small_tile_kernel", "i32_tile_kernel", "splitk_reduce_kernel", "zero_fill_kernel",
            "repack_rows_kernel")
 MFMA_MOP_FLOPS = 512  # flops per unit of SQ_INSTS_VALU_MFMA_MOPS_* (checked against the model in the report)
+SIMDS, XCDS = 1024, 8  # MI355X: 256 CUs x 4 SIMDs, 8 XCDs
 
 
 def read_counters(dirs, skip: int = 2) -> dict:
@@ -139,7 +141,7 @@ def report(w, plan, counters=None, scales=None) -> dict:
     requested = m["bytes_a"] + m["bytes_b"]
     rows = collections.OrderedDict()
     rows["flops (2MNK)"] = (m["flops"], None)
-    rows["executed flops (padding included)"] = (m["executed_flops"], None)
+    rows["executed flops (partial M, N tiles padded)"] = (m["executed_flops"], None)
     rows["requested A bytes (no reuse)"] = (m["bytes_a"], None)
     rows["requested B bytes (no reuse)"] = (m["bytes_b"], None)
     rows["C bytes written"] = (m["bytes_c"], None)
@@ -170,6 +172,12 @@ def report(w, plan, counters=None, scales=None) -> dict:
         if mops:
             meas["MFMA flops (MFMA_MOPS x %d)" % MFMA_MOP_FLOPS] = (mops * MFMA_MOP_FLOPS, "%.4fx executed flops" % (
                 mops * MFMA_MOP_FLOPS / max(m["executed_flops"], 1)))
+        for kern, cs in counters.items():
+            if cs.get("GRBM_GUI_ACTIVE") and "SQ_VALU_MFMA_BUSY_CYCLES" in cs:
+                # busy cycles are summed over the 1024 SIMDs, GRBM_GUI_ACTIVE over the 8 XCDs
+                busy = (cs["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS) / (cs["GRBM_GUI_ACTIVE"] / XCDS)
+                meas["%s: matrix pipe busy (MFMA busy cycles per SIMD / active cycles)" % kern] = (busy, "%.1f%%" % (
+                    100 * busy))
         for kern, cs in counters.items():
             for c, v in sorted(cs.items()):
                 meas["raw %s %s (per dispatch)" % (kern, c)] = (v, None)
