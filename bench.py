@@ -15,9 +15,9 @@ accumulation, bf16 output). Prints ONE JSON line on stdout:
   cpu_baseline the oracle (plain CPU triple loop, binary64 sums) timed on a
                bounded sample of rows of the same product on the host cores
   check        the sampled rows of the GPU result against those oracle rows
-  sclk         the gfx clock and socket power under the same load (amd-smi,
-               sampled while the launches continue after the timed region) and
-               the MFMA peak and fraction at that clock
+  sclk         the gfx clock and socket power under the same load (the driver's metrics
+               table, read in process through amdsmi while the launches continue after
+               the timed region) and the MFMA peak and fraction at that clock
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 """
@@ -65,61 +65,86 @@ def load_traffic(workload: str, sha: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def smi_gfx_clock_mhz():
-    """Current gfx clock of GPU 0 from `amd-smi metric -p -c`, averaged over its XCDs (MHz),
-    the reported maximum clock and the socket power (W); Nones when the tool or its
-    output is not usable."""
-    import subprocess
-
+def smi_reader():
+    """A function returning (gfx clock in MHz averaged over the XCDs, the reported maximum
+    clock, socket power in W) for the GPU torch uses as device 0, read in this process from
+    the driver's metrics table through the amdsmi library (no child process); None when the
+    library or the table is not usable here."""
     try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"], capture_output=True, text=True,
-                           timeout=15)
-        data = json.loads(r.stdout)
-        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
-        clocks = gpu["clock"]
-        cur = [v["clk"]["value"] for k, v in clocks.items() if k.startswith("gfx_") and isinstance(v, dict)]
-        top = [v["max_clk"]["value"] for k, v in clocks.items() if k.startswith("gfx_") and isinstance(v, dict)]
-        cur = [float(x) for x in cur if isinstance(x, (int, float))]
-        top = [float(x) for x in top if isinstance(x, (int, float))]
-        watts = None
+        import amdsmi
+        import torch
+
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        props = torch.cuda.get_device_properties(0)
+        want = tuple(getattr(props, k, None) for k in ("pci_domain_id", "pci_bus_id", "pci_device_id"))
+        handle = None
+        for h in handles:
+            dom, bus, rest = amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")
+            if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                handle = h
+        if handle is None and len(handles) == 1:
+            handle = handles[0]
+        if handle is None:
+            return None
         try:
-            w = gpu["power"]["socket_power"]["value"]
-            watts = float(w) if isinstance(w, (int, float)) else None
-        except (KeyError, TypeError):
-            pass
+            top = float(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["max_clk"])
+        except Exception:
+            top = None
+    except Exception:
+        return None
+
+    def num(x):
+        return float(x) if isinstance(x, (int, float)) and not isinstance(x, bool) else None
+
+    def read():
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+        except Exception:
+            return None, None, None
+        clks = m.get("current_gfxclks")
+        cur = [num(v) for v in clks] if isinstance(clks, (list, tuple)) else []
+        cur = [v for v in cur if v is not None and 0 < v < 10000]  # unused XCD slots read as N/A or 0xFFFF
         if not cur:
             return None, None, None
-        return sum(cur) / len(cur), (max(top) if top else None), watts
-    except Exception:
-        return None, None, None
+        watts = num(m.get("current_socket_power"))
+        if watts is None or watts >= 65535:
+            watts = num(m.get("average_socket_power"))
+        return sum(cur) / len(cur), top, watts
+
+    return read
 
 
-# The driver's metrics table, which amd-smi reads, is refreshed far less often than a launch
-# lasts (in process it changed once in the first 820 ms of load): readings in the first second
-# of the window may still show the clock from before the load, and are left out.
+# The driver's metrics table (what amd-smi shows) is refreshed far less often than a launch
+# lasts (it changed once in the first 820 ms of load): readings in the first second of the
+# window may still show the clock from before the load, and are left out.
 CLOCK_SETTLE_S = 1.0
 
 
 def sample_clock_under_load(step, seconds: float):
-    """Keep launching ``step`` for CLOCK_SETTLE_S + ``seconds`` while sampling the gfx clock
-    and socket power with amd-smi in a second thread; returns the clock samples (MHz), the
-    power samples (W), both read after the first CLOCK_SETTLE_S seconds and while the
-    launches were running, and the reported maximum clock."""
+    """Keep launching ``step`` for CLOCK_SETTLE_S + ``seconds`` while a second thread reads
+    the gfx clock and socket power (smi_reader) back to back; returns the clock samples
+    (MHz), the power samples (W), both read after the first CLOCK_SETTLE_S seconds and while
+    the launches were running, and the reported maximum clock."""
     import threading
 
     import torch
 
     samples, top = [], [None]
     stop = threading.Event()
+    read = smi_reader()
+    if read is None:
+        return [], [], None
 
     def sampler():
         while not stop.is_set():
             t0 = time.perf_counter()
-            mhz, mx, watts = smi_gfx_clock_mhz()
+            mhz, mx, watts = read()
             if mhz is None:
                 return
             samples.append((t0, time.perf_counter(), mhz, watts))
             top[0] = mx
+            time.sleep(0.005)
 
     th = threading.Thread(target=sampler, daemon=True)
     t_keep = time.perf_counter() + CLOCK_SETTLE_S
@@ -216,7 +241,7 @@ def main() -> int:
     # a 22 s target gives about 10-12 s of oracle work
     ap.add_argument("--cpu-seconds", type=float, default=22.0)
     ap.add_argument("--clock-window", type=float, default=2.0,
-                    help="seconds of amd-smi clock readings kept while the launches continue after the timed "
+                    help="seconds of clock readings kept while the launches continue after the timed "
                          "region, after a first second whose readings are left out (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -372,9 +397,8 @@ def main() -> int:
     props = torch.cuda.get_device_properties(0)
     result["device"] = {"arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count}
     result["sclk"] = None
-    # Under rocprofv3 its library is loaded into every process this one starts, and it
-    # would bring up the GPU in the amd-smi child before that child starts its own
-    # interpreter: no clock sampling there.
+    # No clock window under rocprofv3: its launches would add thousands of profiled dispatches
+    # to the counter files.
     profiled = "ROCPROFILER_LIBRARY_CTOR" in os.environ or "ROCPROF_OUTPUT_PATH" in os.environ
     if args.clock_window > 0 and not profiled:
         samples, watts, max_mhz = sample_clock_under_load(step, args.clock_window)
@@ -383,8 +407,9 @@ def main() -> int:
             top = max_mhz or 2400.0
             peak_now = PEAK_MFMA_16BIT_TFLOPS * med / top
             result["sclk"] = {
-                "source": "amd-smi metric -p -c (gfx clock, mean over XCDs; socket power), sampled while the same launches "
-                          "continue for %.1f s after the timed region (readings of the first %.1f s left out)" % (
+                "source": "driver metrics table via amdsmi, in process (gfx clock, mean over XCDs; socket power), read "
+                          "while the same launches continue for %.1f s after the timed region (readings of the first "
+                          "%.1f s left out)" % (
                               CLOCK_SETTLE_S + args.clock_window, CLOCK_SETTLE_S),
                 "median_mhz": med, "min_mhz": float(np.min(samples)), "max_mhz": float(np.max(samples)),
                 "samples": len(samples), "max_clk_mhz": top,
