@@ -214,7 +214,10 @@ gemm_status_t gemm_run_op_noalloc(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_
  * page: the compiler tunes the tile size automatically). Runs every candidate --
  * each macro tile (256x256, 256x128, 128x128, 64x64) with K-slice counts up to 32,
  * the 4-stage twins where they apply, and the 16x16x32 tile for outputs of up to
- * 2^20 elements -- on the caller's buffers on `stream`: one warm-up launch and
+ * 2^20 elements; where an operand's rows are off 128-byte boundaries and the handle
+ * leaves operand copies automatic (gemm_set_repack 0), each macro-tile candidate
+ * also with every subset of those operands copied into aligned rows -- on the
+ * caller's buffers on `stream`: one warm-up launch and
  * `iters` (1..1000) timed launches each, timed with HIP events. BLOCKS until the
  * stream has run them. C receives the product (every candidate computes it). The
  * fastest candidate is written to *best and kept in the handle for this shape

@@ -130,3 +130,31 @@ def test_forced_settings_win_and_nothing_to_tune():
             d.tune(g.h, iters=0)
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("shape", [(1024, 1024, 1000), (520, 1000, 1032)], ids=str)
+def test_tuning_tries_operand_copies(o, shape):
+    """Rows off cache lines (lda = K = 1000, or ldb = N = 1000): the tuner also times
+    the plans with those operands copied into aligned rows; whichever it keeps, the
+    result is the oracle's, and copies only ever cover a misaligned operand."""
+    M, N, K = shape
+    misaligned = (1 if (2 * K) % 128 else 0) | (2 if (2 * N) % 128 else 0)
+    a, b = inputs.random_case(M, N, K, "bf16", seed=M + N)
+    d = Dev(a, b, tgemm.BF16_F32)
+    g = tgemm.Gemm()
+    try:
+        best = d.tune(g.h)
+        assert best["kernel"] == 4 and best["repack"] & ~misaligned == 0, best
+        assert {k: best[k] for k in KEYS} == {k: d.plan(g.h)[k] for k in KEYS}
+        print("%s: tuned plan tile %dx%d split %d stages %d repack %d" % (
+            shape, best["tile_m"], best["tile_n"], best["split_k"], best["stages"], best["repack"]), flush=True)
+        d.c.zero_()
+        d.run(g.h)
+        torch.cuda.synchronize()
+        ref = o.gemm(a, b, "bf16", "f32").view(np.int32)
+        G.compare(d.c.cpu().numpy(), ref, "f32")
+        # a handle that forbids copies tunes without them
+        tgemm.check(tgemm.gemm_set_repack(g.h, -1), "gemm_set_repack")
+        assert d.tune(g.h)["repack"] == 0
+    finally:
+        g.close()

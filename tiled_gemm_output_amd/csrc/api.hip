@@ -36,6 +36,7 @@ struct tune_key_hash {
 struct tune_choice {
   int kernel, tm, tn, tk, split_k, stages;
   int tail_split_k = 0, tail_m0 = 0;  // a split-K tail after the full rounds (the automatic plan's)
+  int repack = -1;                    // operand copies (plan.repack bits), or -1: the automatic plan's
 };
 
 // Scratch memory of gemm_run_op_noalloc: one array on every GPU the library runs on,
@@ -330,6 +331,17 @@ size_t pack_bytes(int repack, const Stored& a, const Stored& b) {
 // row five instead of four).
 bool rows_misaligned(const Stored& x) { return ((uintptr_t)x.base & 127) != 0 || ((x.ld * 2) & 127) != 0; }
 
+// Whether the direct loads still apply with the operands of `bits` (bit 0 A, bit 1 B)
+// copied into aligned rows: every tile offset must stay inside a buffer range.
+bool copies_fit(int bits, int64_t M, int64_t N, int64_t K, const Stored& a, const Stored& b, int bm, int bn, int bk,
+                bool ta, bool tb) {
+  if (bits == 0) return true;
+  const void* aligned = (const void*)(uintptr_t)256;
+  const int64_t lda = (bits & 1) ? packed_ld(a.cols) : a.ld, ldb = (bits & 2) ? packed_ld(b.cols) : b.ld;
+  return vector_ok(M, N, K, (bits & 1) ? aligned : a.base, lda, (bits & 2) ? aligned : b.base, ldb, bm, bn, bk, ta,
+                   tb, true);
+}
+
 // Which operands to copy into aligned rows (bit 0 A, bit 1 B): mode 1 every operand
 // whose rows are off 128-byte boundaries; mode 0 those where the estimated time saved
 // (the operand's share of the product's time) exceeds the copy's time and the copy is
@@ -351,12 +363,7 @@ int choose_repack(int mode, int64_t M, int64_t N, int64_t K, const Stored& a, co
     }
     bits |= 1 << i;
   }
-  // the copies' tile offsets must stay inside a buffer range
-  const uintptr_t aligned = 256;
-  const int64_t lda = (bits & 1) ? packed_ld(a.cols) : a.ld, ldb = (bits & 2) ? packed_ld(b.cols) : b.ld;
-  if (bits && !vector_ok(M, N, K, (const void*)aligned, lda, (const void*)aligned, ldb, bm, bn, bk, ta, tb, true))
-    return 0;
-  return bits;
+  return copies_fit(bits, M, N, K, a, b, bm, bn, bk, ta, tb) ? bits : 0;
 }
 
 // The plan of a tuned choice (vector_loads kept from the automatic plan: it does
@@ -379,6 +386,7 @@ void apply_choice(const tune_choice& c, int64_t M, int64_t N, int64_t K, gemm_pl
   p->grid = cdiv(M, c.tm) * cdiv(N, c.tn);
   p->tail_split_k = c.tail_split_k;
   p->tail_m0 = c.tail_m0;
+  if (c.repack >= 0) p->repack = c.repack;
   (void)K;
 }
 
@@ -841,14 +849,33 @@ gemm_status_t gemm_tune(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t
 
     // Candidates: the automatic plan when it has a split-K tail, every 2-stage macro
     // tile with K-slice counts up to 32 (each slice at least 2 K-tiles), the 4-stage
-    // twins where they apply, and the one-wave 16x16x32 tile for small outputs.
+    // twins where they apply, and the one-wave 16x16x32 tile for small outputs. Where
+    // an operand's rows are off cache lines (and the handle does not force the choice),
+    // each macro-tile candidate is tried with every subset of those operands copied
+    // into aligned rows that keeps the direct loads.
+    const Stored sa{ta ? K : M, ta ? M : K, lda, A, !ta}, sb{tb ? N : K, tb ? K : N, ldb, B, tb};
+    const int misaligned = (base.kernel == 4 && vec && h->repack == 0)
+                               ? ((rows_misaligned(sa) ? 1 : 0) | (rows_misaligned(sb) ? 2 : 0))
+                               : 0;
     std::vector<tune_choice> cand;
-    auto add = [&](const tune_choice& c) {
+    auto add_one = [&](const tune_choice& c) {
       for (const tune_choice& d : cand)
         if (d.kernel == c.kernel && d.tm == c.tm && d.tn == c.tn && d.split_k == c.split_k && d.stages == c.stages &&
-            d.tail_split_k == c.tail_split_k && d.tail_m0 == c.tail_m0)
+            d.tail_split_k == c.tail_split_k && d.tail_m0 == c.tail_m0 && d.repack == c.repack)
           return;
       cand.push_back(c);
+    };
+    auto add = [&](const tune_choice& c) {
+      if (c.kernel != 4 || misaligned == 0) {
+        add_one(c);
+        return;
+      }
+      for (int bits = 0; bits <= 3; ++bits) {
+        if ((bits & ~misaligned) != 0 || !copies_fit(bits, M, N, K, sa, sb, c.tm, c.tn, c.tk, ta, tb)) continue;
+        tune_choice r = c;
+        r.repack = bits;
+        add_one(r);
+      }
     };
     if (base.kernel == 4 && base.tail_split_k > 1)
       add(tune_choice{4, base.tile_m, base.tile_n, base.tile_k, 1, base.stages, base.tail_split_k, base.tail_m0});
