@@ -38,3 +38,19 @@ def test_counters_and_scales(tmp_path):
     assert r["model"]["split-K workspace bytes (written + read)"][0] == 2 * 4 * 4 * 128 * 8192
     text = report.render(r, markdown=True)
     assert text.startswith("### skinny128x8192x8192_bf16: tile 128x128x64") and "| flops (2MNK) |" in text
+
+
+def test_matrix_pipe_busy(tmp_path):
+    """Busy cycles are summed over 1024 SIMDs and GRBM_GUI_ACTIVE over 8 XCDs."""
+    d = str(tmp_path / "mfma")
+    rows = []
+    for _ in range(4):
+        rows += [("macro_tile_kernel", "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 750.0),
+                 ("macro_tile_kernel", "GRBM_GUI_ACTIVE", 8 * 1000.0),
+                 ("macro_tile_kernel", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 1.0)]
+    write_csv(d, "g", rows)
+    c = report.read_counters([d], skip=0)
+    w = inputs.WORKLOADS["square4096_bf16"]
+    r = report.report(w, report.plan_for(w), c, None)
+    key = "macro_tile_kernel: matrix pipe busy (MFMA busy cycles per SIMD / active cycles)"
+    assert abs(r["measured"][key][0] - 0.75) < 1e-12 and r["measured"][key][1] == "75.0%"
