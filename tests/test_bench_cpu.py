@@ -21,3 +21,20 @@ def test_kernel_source_sha_is_stable():
 
     a, b = bench.kernel_source_sha(), bench.kernel_source_sha()
     assert a == b and len(a) == 16
+
+
+def test_clock_reader_is_absent_without_a_gpu():
+    """The in-process metrics reader gives up quietly where no GPU (or no amdsmi) is
+    usable, and the clock window then reports nothing rather than failing."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import torch
+
+    if torch.cuda.is_available():
+        import pytest
+
+        pytest.skip("a GPU is visible")
+    assert bench.smi_reader() is None
+    calls = []
+    assert bench.sample_clock_under_load(lambda: calls.append(1), 0.1) == ([], [], None)
+    assert calls == []  # no launches when there is nothing to read
