@@ -154,8 +154,10 @@ gemm_status_t gemm_create(gemm_handle_t* out);
  * Errors: GEMM_ERR_INVALID_ARG, GEMM_ERR_UNSUPPORTED_DTYPE, GEMM_ERR_UNSUPPORTED_TILE
  * (a forced tile this dtype has no kernel for), GEMM_ERR_OUT_OF_MEMORY (a workspace),
  * GEMM_ERR_HIP (launch failed).
- * Split-K: with the automatic tile choice, a product whose C tiles cannot fill half
+ * Split-K: with the automatic tile choice, a product whose C tiles fill at most half
  * of the GPU and whose K is long is computed in K-slices (gemm_plan reports split_k),
+ * so is one round of 128x128 tiles with a still longer K (two slices, two workgroups
+ * per compute unit),
  * and a last, partly full round of tiles may run as a split-K tail (tail_split_k).
  * The fp32 partial tiles go to a device workspace owned by the handle; operand
  * copies into line-aligned rows (gemm_plan reports repack; see gemm_set_repack) go
@@ -249,7 +251,8 @@ gemm_status_t gemm_set_tile(gemm_handle_t h, int32_t tm, int32_t tn, int32_t tk)
 /* Force the number of K-slices S of later gemm_run calls on this handle that use
  * the macro-tile MFMA kernel (gemm_plan_t.kernel == 4); other kernels ignore it.
  * 0 returns to the library's choice (split only with automatic tiles, when the C
- * tiles cannot fill half of the GPU and K is long), 1 never splits, 2..64 ask for
+ * tiles fill at most half of the GPU, or one round of 128x128 tiles, and K is long),
+ * 1 never splits, 2..64 ask for
  * S slices: each holds cdiv(nk, S) of the nk K-tiles, and S is lowered so that no
  * slice is empty (gemm_plan reports the count used). Split-K needs a workspace of
  * S * M * N * 4 bytes (see gemm_run). Out of range or a bad handle ->

@@ -294,6 +294,34 @@ def test_split_k_forced(h, o, shape, splits):
         check_full(h, o, a, b, dtype, splits=splits)
 
 
+@pytest.mark.parametrize("shape", [(1100, 2000, 8200), (2048, 1024, 8192), (1100, 2000, 4000)], ids=str)
+def test_automatic_split_of_one_round(h, o, shape):
+    """Automatic plans of at most one round of 128x128 tiles: 129-256 tiles with a long
+    reduction are cut in two (two workgroups per compute unit), exactly 128 tiles get
+    the half-chip split, a short reduction none of the pair split. Sampled rows and
+    columns against the oracle: integer-valued inputs bit for bit, N(0, 1) inputs to
+    the accuracy rule."""
+    M, N, K = shape
+    p = plan_of(h, M, N, K, tgemm.BF16_F32)
+    tiles = -(-M // 128) * -(-N // 128)
+    nk = -(-K // 64)
+    print("automatic one-round split %s: tile %dx%d tiles %d split %d stages %d" % (
+        shape, p["tile_m"], p["tile_n"], tiles, p["split_k"], p["stages"]), flush=True)
+    assert (p["tile_m"], p["tile_n"]) == (128, 128)
+    if tiles <= 128:
+        assert p["split_k"] == 256 // tiles
+    elif nk >= 128:
+        assert p["split_k"] == 2 and p["stages"] == 2
+    else:
+        assert p["split_k"] == 1
+    rows, cols = inputs.sample_rows_cols(M, N, seed=11, block=128)
+    a = inputs.draw((M, K), "small_int", "bf16", 201)
+    b = inputs.draw((K, N), "small_int", "bf16", 202)
+    sampled_check(h, o, a, b, tgemm.BF16_F32, rows, cols, exact=True)
+    a, b = inputs.random_case(M, N, K, "bf16", seed=203)
+    sampled_check(h, o, a, b, tgemm.BF16_F32, rows, cols)
+
+
 @pytest.mark.parametrize("splits", [0, 4, 7])
 def test_split_k_integer_inputs_bit_exact(h, o, splits):
     """Integer-valued inputs: every partial sum is exact, so the split result must

@@ -165,6 +165,8 @@ constexpr int kMaxSplits = 64;  // largest K-slice count gemm_set_split_k accept
 constexpr int64_t kDeepMaxWorkgroups = 256;  // one per compute unit of MI355X
 constexpr int64_t kSplitMinKTiles = 32;      // automatic split-K only for long reductions (a second kernel costs
                                              // a few microseconds)
+constexpr int64_t kSplitPairMinKTiles = 128; // ... and for one round of 128x128 tiles, split in two, only when
+                                             // the reduction is longer still
 constexpr int kMaxTuneIters = 1000;                      // timed launches per candidate, at most
 constexpr int64_t kTuneMaxWorkgroups = 8192;             // split candidates beyond this many workgroups are skipped
 constexpr int64_t kTuneSmallTileMaxOutputs = 1 << 20;    // the 16x16x32 tile is tried for outputs up to this size
@@ -460,21 +462,28 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
   } else {
     p.grid = cdiv(M, p.tile_m) * cdiv(N, p.tile_n);
     if (p.grid > kI32Max) return GEMM_ERR_INVALID_ARG;
-    // Split-K (automatic tiles only): when the C tiles cannot fill half of the chip
+    // Split-K (automatic tiles only): when the C tiles fill at most half of the chip
     // and the reduction is long, each tile's K range is cut into slices computed by
     // separate workgroups; their fp32 partial tiles are summed by a second kernel.
-    // A forced slice count (gemm_set_split_k) replaces the heuristic. Slices hold
-    // cdiv(nk, S) K-tiles each, and S is lowered so that none is empty.
+    // One round of 128x128 tiles (at most one per compute unit) with a longer reduction
+    // is cut in two, so that two workgroups share each compute unit (MI355X, bf16,
+    // K = 8192: 1536x2048 62.5 against 73.7 us, 2048x2048 75.4 against 81.9; with
+    // K = 4096 the pair loses at 256 tiles). A forced slice count (gemm_set_split_k)
+    // replaces the heuristic. Slices hold cdiv(nk, S) K-tiles each, and S is lowered
+    // so that none is empty.
     const int64_t nk = cdiv(K, p.tile_k);
     const int fs = h ? h->splits : 0;
     int64_t sk = 1;
     if (p.kernel == 4) {
       if (fs > 0) {
         sk = fs;
-      } else if (!forced && p.grid < 128 && nk >= kSplitMinKTiles) {
+      } else if (!forced && p.grid <= 128 && nk >= kSplitMinKTiles) {
         sk = 256 / p.grid;
         if (sk > 16) sk = 16;
         if (sk > nk / 4) sk = nk / 4;
+      } else if (!forced && p.tile_m == 128 && p.tile_n == 128 && p.grid <= kDeepMaxWorkgroups &&
+                 nk >= kSplitPairMinKTiles) {
+        sk = 2;
       }
     }
     if (sk > nk) sk = nk;
