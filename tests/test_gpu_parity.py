@@ -294,11 +294,12 @@ def test_split_k_forced(h, o, shape, splits):
         check_full(h, o, a, b, dtype, splits=splits)
 
 
-@pytest.mark.parametrize("shape", [(1100, 2000, 8200), (2048, 1024, 8192), (1100, 2000, 4000)], ids=str)
+@pytest.mark.parametrize("shape", [(1100, 2000, 8200), (2048, 1024, 8192), (1100, 2000, 4000), (768, 768, 8192)], ids=str)
 def test_automatic_split_of_one_round(h, o, shape):
     """Automatic plans of at most one round of 128x128 tiles: 129-256 tiles with a long
-    reduction are cut in two (two workgroups per compute unit), exactly 128 tiles get
-    the half-chip split, a short reduction none of the pair split. Sampled rows and
+    reduction are cut in two (two workgroups per compute unit), 128 tiles or fewer get
+    the split that fills the chip (768x768 with 64 K-tiles or more: 128x128 split, not
+    144 unsplit 64x64 tiles), a short reduction none of the pair split. Sampled rows and
     columns against the oracle: integer-valued inputs bit for bit, N(0, 1) inputs to
     the accuracy rule."""
     M, N, K = shape

@@ -242,9 +242,13 @@ int find_macro(int tm, int tn, int tk, int stages = 2) {
 // per CU, 1.86 with one). Tile counts that leave a nearly empty last round lose
 // (3072^3: 144 tiles of 256x256 in one round beat 288 of 256x128 in two). Outputs
 // where 128x128 leaves at least half of the chip idle use 64x64: below 128 such tiles
-// when K is short (no split-K follows; 1024^3 runs in half the time on 64x64), below
-// 64 when K is long (split-K then fills the chip, and a 128-row tile reads B once
-// for outputs of at most 128 rows).
+// when K is short (no split-K follows; 1024^3 runs in half the time on 64x64); below
+// 64 when K is long (32 to 63 K-tiles: split-K then fills the chip, and a 128-row
+// tile reads B once for outputs of at most 128 rows); and with 64 K-tiles or more only
+// where the 64x64 tiles are few enough (at most 128) to be split: from 33 tiles of
+// 128x128 on, those are split instead (768x768x8192: 24.0 us with 128x128 and 7
+// K-slices against 44.8 with 144 unsplit 64x64 tiles; 768x768x2048, with 32 K-tiles,
+// 13.5 us on 64x64 against 17.1 split).
 int auto_macro(int64_t M, int64_t N, int64_t K) {
   constexpr int64_t kCUs = 256;
   const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
@@ -268,7 +272,8 @@ int auto_macro(int64_t M, int64_t N, int64_t K) {
     }
   }
   const int64_t t128 = cdiv(M, 128) * cdiv(N, 128);
-  if (best == 2 && t128 < (cdiv(K, 64) < kSplitMinKTiles ? 128 : 64)) return 3;
+  const int64_t nk = cdiv(K, 64);
+  if (best == 2 && t128 < (nk < kSplitMinKTiles ? 128 : (nk < 2 * kSplitMinKTiles ? 64 : 33))) return 3;
   return best;
 }
 
