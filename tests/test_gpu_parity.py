@@ -323,6 +323,25 @@ def test_automatic_split_of_one_round(h, o, shape):
     sampled_check(h, o, a, b, tgemm.BF16_F32, rows, cols)
 
 
+@pytest.mark.parametrize("shape", [(2600, 1900, 8300), (1000, 1000, 42000)], ids=str)
+def test_automatic_split_of_few_256_tiles(h, o, shape):
+    """At most 96 tiles of 256x256 with slices of at least 40 K-tiles: the automatic
+    plan is 256x256 with S = 256 / tiles (at most 16) K-slices, ragged extents and K
+    tail included. Sampled rows and columns against the oracle (integer-valued inputs
+    bit for bit, N(0, 1) inputs to the accuracy rule)."""
+    M, N, K = shape
+    p = plan_of(h, M, N, K, tgemm.BF16_BF16)
+    tiles = -(-M // 256) * -(-N // 256)
+    print("automatic 256x256 split %s: tiles %d split %d" % (shape, tiles, p["split_k"]), flush=True)
+    assert (p["tile_m"], p["tile_n"]) == (256, 256) and p["split_k"] == min(256 // tiles, 16), p
+    rows, cols = inputs.sample_rows_cols(M, N, seed=13, block=256)
+    a = inputs.draw((M, K), "small_int", "bf16", 211)
+    b = inputs.draw((K, N), "small_int", "bf16", 212)
+    sampled_check(h, o, a, b, tgemm.BF16_BF16, rows, cols, exact=True)
+    a, b = inputs.random_case(M, N, K, "bf16", seed=213)
+    sampled_check(h, o, a, b, tgemm.BF16_BF16, rows, cols)
+
+
 @pytest.mark.parametrize("splits", [0, 4, 7])
 def test_split_k_integer_inputs_bit_exact(h, o, splits):
     """Integer-valued inputs: every partial sum is exact, so the split result must

@@ -167,6 +167,12 @@ constexpr int64_t kSplitMinKTiles = 32;      // automatic split-K only for long 
                                              // a few microseconds)
 constexpr int64_t kSplitPairMinKTiles = 128; // ... and for one round of 128x128 tiles, split in two, only when
                                              // the reduction is longer still
+// Few 256x256 tiles (at most this many) with a long reduction run as 256x256 split-K when
+// every slice keeps at least kSplit256MinSliceKTiles K-tiles (MI355X, bf16: 3072x1536x8192
+// 82.3 against 94.1 us on 128x128, 2048x2048x16384 127.6 against 138.9; with 32 K-tiles per
+// slice, 2048x2048x8192, 128x128 cut in two is as fast).
+constexpr int64_t kSplit256MaxTiles = 96;
+constexpr int64_t kSplit256MinSliceKTiles = 40;
 constexpr int kMaxTuneIters = 1000;                      // timed launches per candidate, at most
 constexpr int64_t kTuneMaxWorkgroups = 8192;             // split candidates beyond this many workgroups are skipped
 constexpr int64_t kTuneSmallTileMaxOutputs = 1 << 20;    // the 16x16x32 tile is tried for outputs up to this size
@@ -253,6 +259,13 @@ int auto_macro(int64_t M, int64_t N, int64_t K) {
   constexpr int64_t kCUs = 256;
   const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
   if (t256 >= kCUs || t256 == 0) return 0;  // an empty output launches nothing
+  // Few 256x256 tiles and a long reduction: 256x256 cut into S = 256 / tiles K-slices
+  // (the split-K rule below), when each slice keeps at least 40 K-tiles.
+  const int64_t nk = cdiv(K, 64);
+  if (t256 <= kSplit256MaxTiles && nk >= kSplitPairMinKTiles) {
+    const int64_t S = kCUs / t256 < 16 ? kCUs / t256 : 16;
+    if (nk / S >= kSplit256MinSliceKTiles) return 0;
+  }
   struct Cand {
     int shape, bm, bn, occ;  // occ: workgroups that fit on one CU
     double f1, f2;           // relative cost per unit of work with 1 and with 2+ workgroups per CU
@@ -272,7 +285,6 @@ int auto_macro(int64_t M, int64_t N, int64_t K) {
     }
   }
   const int64_t t128 = cdiv(M, 128) * cdiv(N, 128);
-  const int64_t nk = cdiv(K, 64);
   if (best == 2 && t128 < (nk < kSplitMinKTiles ? 128 : (nk < 2 * kSplitMinKTiles ? 64 : 33))) return 3;
   return best;
 }
