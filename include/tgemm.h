@@ -220,9 +220,12 @@ gemm_status_t gemm_run_op_noalloc(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_
  * leaves operand copies automatic (gemm_set_repack 0), each macro-tile candidate
  * also with every subset of those operands copied into aligned rows -- on the
  * caller's buffers on `stream`: one warm-up launch and
- * `iters` (1..1000) timed launches each, timed with HIP events. BLOCKS until the
- * stream has run them. C receives the product (every candidate computes it). The
- * fastest candidate is written to *best and kept in the handle for this shape
+ * `iters` (1..1000) timed launches each, timed with HIP events; then the three
+ * fastest and the automatic plan again, twice, in one order and its reverse (the
+ * clock drifts under sustained load), and a candidate replaces the automatic plan
+ * only if it is more than 1% faster over both. BLOCKS until the stream has run
+ * them. C receives the product (every candidate computes it). The chosen candidate
+ * is written to *best and kept in the handle for this shape
  * (op_a, op_b, M, N, K, dtype and whether 16-byte loads apply): later gemm_run /
  * gemm_run_op / gemm_plan calls on the handle with that shape use it. A forced tile
  * or K-slice count (gemm_set_tile, gemm_set_split_k) takes precedence over a tuned

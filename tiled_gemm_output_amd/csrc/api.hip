@@ -3,6 +3,7 @@
 // call; launches are asynchronous on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -933,25 +934,61 @@ gemm_status_t gemm_tune(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t
     } ev;
     if (hipEventCreate(&ev.e0) != hipSuccess || hipEventCreate(&ev.e1) != hipSuccess) return GEMM_ERR_HIP;
     hipEvent_t e0 = ev.e0, e1 = ev.e1;
-    float best_ms = 0.0f;
-    int best_i = -1;
-    for (size_t i = 0; i < cand.size() && st == GEMM_OK; ++i) {
+    // Time candidate i: one warm-up launch (which also sizes any workspace), then
+    // `reps` launches between two events.
+    auto time_one = [&](size_t i, int reps, float* ms) -> gemm_status_t {
       gemm_plan_t p = base;
       apply_choice(cand[i], M, N, K, &p);
-      st = launch_plan(wsrc, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, s);  // warm-up (and workspace)
-      if (st != GEMM_OK) break;
-      if (hipEventRecord(e0, s) != hipSuccess) st = GEMM_ERR_HIP;
-      for (int r = 0; r < iters && st == GEMM_OK; ++r)
-        st = launch_plan(wsrc, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, s);
-      float ms = 0.0f;
-      if (st == GEMM_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
-                            hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
-        st = GEMM_ERR_HIP;
-      if (st == GEMM_OK && (best_i < 0 || ms < best_ms)) {
-        best_ms = ms;
-        best_i = (int)i;
+      gemm_status_t r = launch_plan(wsrc, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, s);
+      if (r != GEMM_OK) return r;
+      if (hipEventRecord(e0, s) != hipSuccess) return GEMM_ERR_HIP;
+      for (int k = 0; k < reps && r == GEMM_OK; ++k)
+        r = launch_plan(wsrc, p, ta, tb, M, N, K, A, lda, B, ldb, C, ldc, (int)dtype, s);
+      if (r != GEMM_OK) return r;
+      if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+          hipEventElapsedTime(ms, e0, e1) != hipSuccess)
+        return GEMM_ERR_HIP;
+      return GEMM_OK;
+    };
+    std::vector<float> first(cand.size(), 0.0f);
+    for (size_t i = 0; i < cand.size() && st == GEMM_OK; ++i) st = time_one(i, iters, &first[i]);
+    if (st != GEMM_OK) return st;
+    // The card's clock drifts under sustained load, so one pass in a fixed order can
+    // favour the candidates that ran early or late. The three fastest of the first
+    // pass and the automatic plan are timed again, in one order and then in the
+    // reverse one; a candidate replaces the automatic plan only if it is more than
+    // 1% faster over both.
+    int auto_i = -1;
+    for (size_t i = 0; i < cand.size(); ++i) {
+      const tune_choice& c = cand[i];
+      if (c.kernel == base.kernel && c.tm == base.tile_m && c.tn == base.tile_n && c.split_k == base.split_k &&
+          c.stages == base.stages && c.tail_split_k == base.tail_split_k && c.tail_m0 == base.tail_m0 &&
+          (c.repack < 0 || c.repack == base.repack)) {
+        auto_i = (int)i;
+        break;
       }
     }
+    std::vector<int> fin;
+    {
+      std::vector<int> order(cand.size());
+      for (size_t i = 0; i < cand.size(); ++i) order[i] = (int)i;
+      std::sort(order.begin(), order.end(), [&](int x, int y) { return first[x] < first[y]; });
+      for (size_t i = 0; i < order.size() && i < 3; ++i) fin.push_back(order[i]);
+      if (auto_i >= 0 && std::find(fin.begin(), fin.end(), auto_i) == fin.end()) fin.push_back(auto_i);
+    }
+    std::vector<double> total(cand.size(), 0.0);
+    for (int pass = 0; pass < 2 && st == GEMM_OK; ++pass)
+      for (size_t n = 0; n < fin.size() && st == GEMM_OK; ++n) {
+        const int i = fin[pass == 0 ? n : fin.size() - 1 - n];
+        float ms = 0.0f;
+        st = time_one((size_t)i, iters, &ms);
+        total[i] += ms;
+      }
+    if (st != GEMM_OK) return st;
+    int best_i = fin[0];
+    for (int i : fin)
+      if (total[i] < total[best_i]) best_i = i;
+    if (auto_i >= 0 && total[best_i] > 0.99 * total[auto_i]) best_i = auto_i;
     if (st != GEMM_OK) return st;
     h->tuned[key] = cand[best_i];
     gemm_plan_t p = base;
