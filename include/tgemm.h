@@ -156,8 +156,8 @@ gemm_status_t gemm_create(gemm_handle_t* out);
  * GEMM_ERR_HIP (launch failed).
  * Split-K: with the automatic tile choice, a product whose C tiles fill at most half
  * of the GPU and whose K is long is computed in K-slices (gemm_plan reports split_k),
- * so is one round of 128x128 tiles with a still longer K (two slices, two workgroups
- * per compute unit),
+ * so is one round of 128x128 tiles with a still longer K (slices enough for two
+ * workgroups per compute unit),
  * and a last, partly full round of tiles may run as a split-K tail (tail_split_k).
  * The fp32 partial tiles go to a device workspace owned by the handle; operand
  * copies into line-aligned rows (gemm_plan reports repack; see gemm_set_repack) go

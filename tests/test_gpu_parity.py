@@ -296,10 +296,11 @@ def test_split_k_forced(h, o, shape, splits):
 
 @pytest.mark.parametrize("shape", [(1100, 2000, 8200), (2048, 1024, 8192), (1100, 2000, 4000), (768, 768, 8192)], ids=str)
 def test_automatic_split_of_one_round(h, o, shape):
-    """Automatic plans of at most one round of 128x128 tiles: 129-256 tiles with a long
-    reduction are cut in two (two workgroups per compute unit), 128 tiles or fewer get
-    the split that fills the chip (768x768 with 64 K-tiles or more: 128x128 split, not
-    144 unsplit 64x64 tiles), a short reduction none of the pair split. Sampled rows and
+    """Automatic plans of at most one round of 128x128 tiles: 65-256 tiles with a long
+    reduction are cut into 512 / tiles slices (two workgroups on every compute unit),
+    fewer tiles get the split that fills the chip once (768x768 with 64 K-tiles or
+    more: 128x128 split, not 144 unsplit 64x64 tiles), and more than 128 tiles with a
+    short reduction are not split. Sampled rows and
     columns against the oracle: integer-valued inputs bit for bit, N(0, 1) inputs to
     the accuracy rule."""
     M, N, K = shape
@@ -309,10 +310,10 @@ def test_automatic_split_of_one_round(h, o, shape):
     print("automatic one-round split %s: tile %dx%d tiles %d split %d stages %d" % (
         shape, p["tile_m"], p["tile_n"], tiles, p["split_k"], p["stages"]), flush=True)
     assert (p["tile_m"], p["tile_n"]) == (128, 128)
-    if tiles <= 128:
+    if 64 < tiles <= 256 and nk >= 128:
+        assert p["split_k"] == 512 // tiles and p["stages"] == 2
+    elif tiles <= 128:
         assert p["split_k"] == 256 // tiles
-    elif nk >= 128:
-        assert p["split_k"] == 2 and p["stages"] == 2
     else:
         assert p["split_k"] == 1
     rows, cols = inputs.sample_rows_cols(M, N, seed=11, block=128)

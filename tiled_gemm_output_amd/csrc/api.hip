@@ -483,10 +483,12 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
     // Split-K (automatic tiles only): when the C tiles fill at most half of the chip
     // and the reduction is long, each tile's K range is cut into slices computed by
     // separate workgroups; their fp32 partial tiles are summed by a second kernel.
-    // One round of 128x128 tiles (at most one per compute unit) with a longer reduction
-    // is cut in two, so that two workgroups share each compute unit (MI355X, bf16,
-    // K = 8192: 1536x2048 62.5 against 73.7 us, 2048x2048 75.4 against 81.9; with
-    // K = 4096 the pair loses at 256 tiles). A forced slice count (gemm_set_split_k)
+    // 65-256 tiles of 128x128 with a longer reduction are cut into 512 / tiles slices,
+    // so that two workgroups share every compute unit (MI355X, bf16, K = 8192:
+    // 1536x1536 53.6 against 62.5 us with two slices, 1280x1280 41.8 against 46.5,
+    // 2048x2048 75.4 against 81.9 unsplit; with K = 4096 the split loses at 256 tiles,
+    // and up to 64 tiles one workgroup per unit, with the deeper pipeline, is as fast).
+    // A forced slice count (gemm_set_split_k)
     // replaces the heuristic. Slices hold cdiv(nk, S) K-tiles each, and S is lowered
     // so that none is empty.
     const int64_t nk = cdiv(K, p.tile_k);
@@ -495,13 +497,13 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
     if (p.kernel == 4) {
       if (fs > 0) {
         sk = fs;
+      } else if (!forced && p.tile_m == 128 && p.tile_n == 128 && p.grid > 64 && p.grid <= kDeepMaxWorkgroups &&
+                 nk >= kSplitPairMinKTiles) {
+        sk = 2 * kDeepMaxWorkgroups / p.grid;  // two workgroups on every compute unit
       } else if (!forced && p.grid <= 128 && nk >= kSplitMinKTiles) {
         sk = 256 / p.grid;
         if (sk > 16) sk = 16;
         if (sk > nk / 4) sk = nk / 4;
-      } else if (!forced && p.tile_m == 128 && p.tile_n == 128 && p.grid <= kDeepMaxWorkgroups &&
-                 nk >= kSplitPairMinKTiles) {
-        sk = 2;
       }
     }
     if (sk > nk) sk = nk;
