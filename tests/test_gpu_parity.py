@@ -294,28 +294,22 @@ def test_split_k_forced(h, o, shape, splits):
         check_full(h, o, a, b, dtype, splits=splits)
 
 
-@pytest.mark.parametrize("shape", [(1100, 2000, 8200), (2048, 1024, 8192), (1100, 2000, 4000), (768, 768, 8192)], ids=str)
-def test_automatic_split_of_one_round(h, o, shape):
-    """Automatic plans of at most one round of 128x128 tiles: 65-256 tiles with a long
-    reduction are cut into 512 / tiles slices (two workgroups on every compute unit),
-    fewer tiles get the split that fills the chip once (768x768 with 64 K-tiles or
-    more: 128x128 split, not 144 unsplit 64x64 tiles), and more than 128 tiles with a
-    short reduction are not split. Sampled rows and
+@pytest.mark.parametrize("shape,splits", [((1100, 2000, 8200), 3), ((2048, 1024, 8192), 4), ((1100, 2000, 4000), 3),
+                                          ((2048, 2048, 4096), 1), ((768, 768, 8192), 7), ((128, 8192, 8192), 4)],
+                         ids=str)
+def test_automatic_split_of_one_round(h, o, shape, splits):
+    """Automatic plans of at most one round of 128x128 tiles take the K-slice count of
+    the library's estimate: 144 tiles over 129 or 63 K-tiles in 3 slices, 128 tiles
+    over 128 K-tiles in 4 (two workgroups on every compute unit), a full round over 64
+    K-tiles unsplit, 768x768 with 128 K-tiles as 36 tiles of 128x128 in 7 slices (not
+    144 unsplit 64x64 tiles), the HBM-bound 128-row product in 4. Sampled rows and
     columns against the oracle: integer-valued inputs bit for bit, N(0, 1) inputs to
     the accuracy rule."""
     M, N, K = shape
     p = plan_of(h, M, N, K, tgemm.BF16_F32)
-    tiles = -(-M // 128) * -(-N // 128)
-    nk = -(-K // 64)
-    print("automatic one-round split %s: tile %dx%d tiles %d split %d stages %d" % (
-        shape, p["tile_m"], p["tile_n"], tiles, p["split_k"], p["stages"]), flush=True)
-    assert (p["tile_m"], p["tile_n"]) == (128, 128)
-    if 64 < tiles <= 256 and nk >= 128:
-        assert p["split_k"] == 512 // tiles and p["stages"] == 2
-    elif tiles <= 128:
-        assert p["split_k"] == 256 // tiles
-    else:
-        assert p["split_k"] == 1
+    print("automatic one-round split %s: tile %dx%d split %d stages %d" % (
+        shape, p["tile_m"], p["tile_n"], p["split_k"], p["stages"]), flush=True)
+    assert (p["tile_m"], p["tile_n"]) == (128, 128) and p["split_k"] == splits, p
     rows, cols = inputs.sample_rows_cols(M, N, seed=11, block=128)
     a = inputs.draw((M, K), "small_int", "bf16", 201)
     b = inputs.draw((K, N), "small_int", "bf16", 202)

@@ -166,13 +166,13 @@ constexpr int kMaxSplits = 64;  // largest K-slice count gemm_set_split_k accept
 constexpr int64_t kDeepMaxWorkgroups = 256;  // one per compute unit of MI355X
 constexpr int64_t kSplitMinKTiles = 32;      // automatic split-K only for long reductions (a second kernel costs
                                              // a few microseconds)
-constexpr int64_t kSplitPairMinKTiles = 128; // ... and for one round of 128x128 tiles, split in two, only when
-                                             // the reduction is longer still
 // Few 256x256 tiles (at most this many) with a long reduction run as 256x256 split-K when
 // every slice keeps at least kSplit256MinSliceKTiles K-tiles (MI355X, bf16: 3072x1536x8192
-// 82.3 against 94.1 us on 128x128, 2048x2048x16384 127.6 against 138.9; with 32 K-tiles per
-// slice, 2048x2048x8192, 128x128 cut in two is as fast).
-constexpr int64_t kSplit256MaxTiles = 96;
+// 82.3 against 94.1 us on 128x128, 2048x2048x16384 127.6 against 138.9, 729x9340x19152
+// (111 tiles, 2 slices) 280.2 against 333.0, 8954x586x5871 (105 tiles, 2 slices of 46
+// K-tiles) 96.4 against 107.6; with 32 K-tiles per slice, 2048x2048x8192, 128x128 cut in
+// two is as fast).
+constexpr int64_t kSplit256MaxTiles = 128;
 constexpr int64_t kSplit256MinSliceKTiles = 40;
 constexpr int kMaxTuneIters = 1000;                      // timed launches per candidate, at most
 constexpr int64_t kTuneMaxWorkgroups = 8192;             // split candidates beyond this many workgroups are skipped
@@ -263,7 +263,7 @@ int auto_macro(int64_t M, int64_t N, int64_t K) {
   // Few 256x256 tiles and a long reduction: 256x256 cut into S = 256 / tiles K-slices
   // (the split-K rule below), when each slice keeps at least 40 K-tiles.
   const int64_t nk = cdiv(K, 64);
-  if (t256 <= kSplit256MaxTiles && nk >= kSplitPairMinKTiles) {
+  if (t256 <= kSplit256MaxTiles) {
     const int64_t S = kCUs / t256 < 16 ? kCUs / t256 : 16;
     if (nk / S >= kSplit256MinSliceKTiles) return 0;
   }
@@ -287,6 +287,29 @@ int auto_macro(int64_t M, int64_t N, int64_t K) {
   }
   const int64_t t128 = cdiv(M, 128) * cdiv(N, 128);
   if (best == 2 && t128 < (nk < kSplitMinKTiles ? 128 : (nk < 2 * kSplitMinKTiles ? 64 : 33))) return 3;
+  return best;
+}
+
+// K-slices for one round of T <= 256 tiles of 128x128 over nk K-tiles: the count with
+// the lowest estimated time, 1 (no split) included. MI355X, bf16, measured: a K-step of
+// a workgroup alone on its compute unit ~0.62 us, of two sharing one ~0.91 us; the
+// S x M x N fp32 partial tiles are written and read back at ~4 TB/s, and the reduction
+// adds ~2 us. At most 512 workgroups (two per unit), 16 slices and nk / 4. (The
+// estimate picks, e.g., 3 slices at 1536x1536x8192, 53.6 us against 62.5 with 2 and
+// 79 unsplit; 4 at 2048x1024x8192, 44.6 against 47.5 with 2; none at 2048x2048x4096,
+// 40.1 against 46.0 with 2.)
+int64_t split_one_round_128(int64_t T, int64_t nk, int64_t M, int64_t N) {
+  constexpr double kAlone = 0.62e-6, kShared = 0.91e-6, kPartialBytesPerSecond = 4.0e12, kReduce = 2.0e-6;
+  int64_t best = 1;
+  double best_t = (double)nk * kAlone;
+  for (int64_t S = 2; S <= 16 && S <= nk / 4 && T * S <= 2 * kDeepMaxWorkgroups; ++S) {
+    const double t = (double)cdiv(nk, S) * (T * S <= kDeepMaxWorkgroups ? kAlone : kShared) +
+                     (double)S * (double)M * (double)N * 8.0 / kPartialBytesPerSecond + kReduce;
+    if (t < best_t) {
+      best_t = t;
+      best = S;
+    }
+  }
   return best;
 }
 
@@ -483,12 +506,8 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
     // Split-K (automatic tiles only): when the C tiles fill at most half of the chip
     // and the reduction is long, each tile's K range is cut into slices computed by
     // separate workgroups; their fp32 partial tiles are summed by a second kernel.
-    // 65-256 tiles of 128x128 with a longer reduction are cut into 512 / tiles slices,
-    // so that two workgroups share every compute unit (MI355X, bf16, K = 8192:
-    // 1536x1536 53.6 against 62.5 us with two slices, 1280x1280 41.8 against 46.5,
-    // 2048x2048 75.4 against 81.9 unsplit; with K = 4096 the split loses at 256 tiles,
-    // and up to 64 tiles one workgroup per unit, with the deeper pipeline, is as fast).
-    // A forced slice count (gemm_set_split_k)
+    // One round of 128x128 tiles (both M and N spanning several) takes the slice count
+    // of split_one_round_128's estimate. A forced slice count (gemm_set_split_k)
     // replaces the heuristic. Slices hold cdiv(nk, S) K-tiles each, and S is lowered
     // so that none is empty.
     const int64_t nk = cdiv(K, p.tile_k);
@@ -497,9 +516,9 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
     if (p.kernel == 4) {
       if (fs > 0) {
         sk = fs;
-      } else if (!forced && p.tile_m == 128 && p.tile_n == 128 && p.grid > 64 && p.grid <= kDeepMaxWorkgroups &&
-                 nk >= kSplitPairMinKTiles) {
-        sk = 2 * kDeepMaxWorkgroups / p.grid;  // two workgroups on every compute unit
+      } else if (!forced && p.tile_m == 128 && p.tile_n == 128 && p.grid <= kDeepMaxWorkgroups && M > 128 &&
+                 N > 128 && nk >= kSplitMinKTiles) {
+        sk = split_one_round_128(p.grid, nk, M, N);
       } else if (!forced && p.grid <= 128 && nk >= kSplitMinKTiles) {
         sk = 256 / p.grid;
         if (sk > 16) sk = 16;
