@@ -1,0 +1,38 @@
+"""The automatic plan for shapes whose choice was settled by measurement on MI355X
+(host only: automatic plans need no device). Each row is a shape, the plan the library
+picks for it, and what that plan measured against the alternative it replaced (bf16,
+microseconds per call, one box); a change of rule that moves one of them should come
+with new measurements."""
+import pytest
+
+from tiled_gemm_output_amd import tgemm
+
+# (M, N, K) -> (tile_m, tile_n, split_k, stages, tail_split_k)
+CHOICES = [
+    ((8192, 8192, 8192), (256, 256, 1, 2, 0)),       # the 256x256 tile from one full round on
+    ((4096, 4096, 4096), (256, 256, 1, 2, 0)),
+    ((16384, 1024, 8192), (256, 256, 1, 2, 0)),
+    ((6000, 6000, 6000), (256, 256, 1, 2, 3)),       # partly full last round as a split-K tail
+    ((128, 8192, 8192), (128, 128, 4, 4, 0)),        # HBM-bound: 4 slices, one per CU, 4 stages (34.7 vs 39.8 with 8)
+    ((2048, 1024, 8192), (128, 128, 4, 2, 0)),       # 128 tiles: 44.6 (was 71.7 unsplit)
+    ((1536, 1536, 8192), (128, 128, 3, 2, 0)),       # 144 tiles: 53.3 (64.2 with 2 slices)
+    ((1280, 1280, 8192), (128, 128, 5, 2, 0)),       # 41.4 (47.9 with 2)
+    ((2048, 2048, 8192), (128, 128, 2, 2, 0)),       # 75.4 (81.9 unsplit)
+    ((2048, 2048, 4096), (128, 128, 1, 4, 0)),       # 40.1 (46.0 with 2)
+    ((6713, 307, 3517), (128, 128, 3, 2, 0)),        # 43.3 (49.8 unsplit)
+    ((768, 768, 8192), (128, 128, 7, 4, 0)),         # 24.0 (44.8 as 144 unsplit 64x64 tiles)
+    ((768, 768, 2048), (64, 64, 1, 4, 0)),           # 13.5 (17.1 as 128x128 split)
+    ((3072, 1536, 8192), (256, 256, 3, 2, 0)),       # 84.5 (102.7 as 128x128)
+    ((8954, 586, 5871), (256, 256, 2, 2, 0)),        # 97.1 (108.9 as 128x128)
+    ((1024, 1024, 65536), (256, 256, 16, 2, 0)),     # 154.4 (172.7 as 128x128 in 4)
+    ((512, 2048, 8192), (128, 128, 4, 4, 0)),        # 32.1 (33.5 with 8 slices, two per CU)
+    ((1024, 1024, 1024), (64, 64, 1, 4, 0)),         # short K: 64x64
+]
+
+
+@pytest.mark.parametrize("shape,want", CHOICES, ids=str)
+def test_automatic_plan(shape, want):
+    M, N, K = shape
+    p = tgemm.gemm_plan(None, M, N, K, 1 << 20, K, 1 << 21, N, 1 << 22, N, tgemm.BF16_BF16)
+    got = (p["tile_m"], p["tile_n"], p["split_k"], p["stages"], p["tail_split_k"])
+    assert got == want, (shape, p)
