@@ -944,6 +944,10 @@ gemm_status_t gemm_tune(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t
     if (M * N <= kTuneSmallTileMaxOutputs && vector_ok(M, N, K, A, lda, B, ldb, 16, 16, 32, ta, tb, false) == vec)
       add(tune_choice{3, 16, 16, 32, 1, 2});
 
+    if (cand.empty()) {  // nothing to measure (no tile keeps the plan's loader): the automatic plan
+      *best = base;
+      return GEMM_OK;
+    }
     hipStream_t s = (hipStream_t)stream;
     HandleWs wsrc(h);
     struct Events {  // destroyed on every way out, an exception included
