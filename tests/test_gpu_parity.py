@@ -295,14 +295,17 @@ def test_split_k_forced(h, o, shape, splits):
 
 
 @pytest.mark.parametrize("shape,splits", [((1100, 2000, 8200), 3), ((2048, 1024, 8192), 4), ((1100, 2000, 4000), 3),
-                                          ((2048, 2048, 4096), 1), ((768, 768, 8192), 7), ((128, 8192, 8192), 4)],
+                                          ((2048, 2048, 4096), 1), ((768, 768, 8192), 7), ((128, 8192, 8192), 4),
+                                          ((257, 2440, 3976), 4), ((251, 2033, 11048), 8)],
                          ids=str)
 def test_automatic_split_of_one_round(h, o, shape, splits):
     """Automatic plans of at most one round of 128x128 tiles take the K-slice count of
     the library's estimate: 144 tiles over 129 or 63 K-tiles in 3 slices, 128 tiles
     over 128 K-tiles in 4 (two workgroups on every compute unit), a full round over 64
     K-tiles unsplit, 768x768 with 128 K-tiles as 36 tiles of 128x128 in 7 slices (not
-    144 unsplit 64x64 tiles), the HBM-bound 128-row product in 4. Sampled rows and
+    144 unsplit 64x64 tiles), the HBM-bound 128-row product in 4; 257 x 2440 over 63
+    K-tiles as 60 tiles in 4 slices and 251 x 2033 over 173 K-tiles as 32 tiles in 8
+    (not 64x64 tiles; one-row and ragged last tile rows). Sampled rows and
     columns against the oracle: integer-valued inputs bit for bit, N(0, 1) inputs to
     the accuracy rule."""
     M, N, K = shape
@@ -320,7 +323,7 @@ def test_automatic_split_of_one_round(h, o, shape, splits):
 
 @pytest.mark.parametrize("shape", [(2600, 1900, 8300), (1000, 1000, 42000)], ids=str)
 def test_automatic_split_of_few_256_tiles(h, o, shape):
-    """At most 96 tiles of 256x256 with slices of at least 40 K-tiles: the automatic
+    """At most 128 tiles of 256x256 with slices of at least 40 K-tiles: the automatic
     plan is 256x256 with S = 256 / tiles (at most 16) K-slices, ragged extents and K
     tail included. Sampled rows and columns against the oracle (integer-valued inputs
     bit for bit, N(0, 1) inputs to the accuracy rule)."""

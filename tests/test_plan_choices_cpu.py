@@ -27,6 +27,13 @@ CHOICES = [
     ((1024, 1024, 65536), (256, 256, 16, 2, 0)),     # 154.4 (172.7 as 128x128 in 4)
     ((512, 2048, 8192), (128, 128, 4, 4, 0)),        # 32.1 (33.5 with 8 slices, two per CU)
     ((1024, 1024, 1024), (64, 64, 1, 4, 0)),         # short K: 64x64
+    ((257, 2440, 3976), (128, 128, 4, 4, 0)),        # 60 tiles: 20.4 (27.2 as 195 unsplit 64x64 tiles)
+    ((600, 1400, 4000), (128, 128, 4, 4, 0)),        # 21.2 (27.3 as 220 unsplit 64x64)
+    ((251, 2033, 11048), (128, 128, 8, 4, 0)),       # 32 tiles: 29.9 (39.1 as 64x64 in 2 slices)
+    ((512, 1024, 8192), (128, 128, 8, 4, 0)),        # 23.5 (27.2 as 64x64 in 2)
+    ((1337, 272, 3365), (64, 64, 2, 4, 0)),          # 33 tiles over 53 K-tiles: 16.6 (17.6 as 128x128 in 6)
+    ((633, 542, 3251), (64, 64, 2, 4, 0)),           # 16.5 (18.2 as 128x128 in 6)
+    ((512, 512, 8192), (64, 64, 4, 4, 0)),           # 16 tiles: 18.1 (20.2 as 128x128 in 12)
 ]
 
 

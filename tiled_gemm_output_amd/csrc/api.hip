@@ -255,7 +255,13 @@ int find_macro(int tm, int tn, int tk, int stages = 2) {
 // where the 64x64 tiles are few enough (at most 128) to be split: from 33 tiles of
 // 128x128 on, those are split instead (768x768x8192: 24.0 us with 128x128 and 7
 // K-slices against 44.8 with 144 unsplit 64x64 tiles; 768x768x2048, with 32 K-tiles,
-// 13.5 us on 64x64 against 17.1 split).
+// 13.5 us on 64x64 against 17.1 split). With both sides over 128 rows and at least
+// 48 K-tiles, a round of 128x128 tiles is split by the one-round estimate below, and
+// that beats 64x64 from 36 such tiles on below 64 K-tiles and from 25 on above
+// (257x2440x3976: 20.4 us on 60 tiles in 4 K-slices against 27.2 for 195 unsplit
+// 64x64 tiles; 251x2033x11048: 29.9 on 32 tiles in 8 slices against 39.1 for 128
+// 64x64 tiles in 2; but 1337x272x3365, 33 tiles over 53 K-tiles: 16.6 on 64x64
+// against 17.6, and 512x512x8192, 16 tiles: 18.1 on 64x64 against 20.2).
 int auto_macro(int64_t M, int64_t N, int64_t K) {
   constexpr int64_t kCUs = 256;
   const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
@@ -286,7 +292,12 @@ int auto_macro(int64_t M, int64_t N, int64_t K) {
     }
   }
   const int64_t t128 = cdiv(M, 128) * cdiv(N, 128);
-  if (best == 2 && t128 < (nk < kSplitMinKTiles ? 128 : (nk < 2 * kSplitMinKTiles ? 64 : 33))) return 3;
+  const bool round128_split = M > 128 && N > 128 && 2 * nk >= 3 * kSplitMinKTiles;
+  const int64_t max64 = nk < kSplitMinKTiles       ? 128
+                        : round128_split           ? (nk < 2 * kSplitMinKTiles ? 36 : 25)
+                        : nk < 2 * kSplitMinKTiles ? 64
+                                                   : 33;
+  if (best == 2 && t128 < max64) return 3;
   return best;
 }
 
