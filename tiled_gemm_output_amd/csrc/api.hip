@@ -739,7 +739,11 @@ gemm_status_t launch_mfma_part(WsSource& wsrc, const gemm_plan_t& p, int splits,
   a.ldc = ldc;
   a.tiles_m = (int)cdiv(M, p.tile_m);
   a.tiles_n = (int)cdiv(N, p.tile_n);
-  a.group_m = a.tiles_m < 4 ? a.tiles_m : 4;
+  // With one tile row or one tile column no tiles share a panel: keep the hardware's
+  // order, so that the tiles an XCD runs at once lie far apart along the streamed
+  // operand (MI355X, 128x8192x8192 in 4 K-slices: 26.8 against 30.1 us for the GEMM
+  // kernel with consecutive tiles on one XCD; 8192x128x8192 unchanged).
+  a.group_m = (a.tiles_m == 1 || a.tiles_n == 1) ? 0 : (a.tiles_m < 4 ? a.tiles_m : 4);
   const int64_t nk = cdiv(K, p.tile_k);
   a.kt_per_split = (int)cdiv(nk, splits);
   a.split_stride = (int64_t)M * N;

@@ -110,8 +110,16 @@ __device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
 // resident on one XCD get consecutive ids, then walk the C tiles in groups of
 // `group_m` tile rows (column by column inside a group), so that tiles running
 // at the same time on one XCD share A row panels and B column panels in its L2.
+// group_m = 0 keeps the hardware's order (tile = workgroup id, M fastest): with a
+// single tile row or column there is no panel to share, and consecutive tiles on
+// different XCDs spread each XCD's requests over the whole streamed operand.
 __device__ __forceinline__ void schedule_tile(int wg, int num_wg, int tiles_m, int group_m, int& tile_m,
                                               int& tile_n) {
+  if (group_m == 0) {
+    tile_m = wg % tiles_m;
+    tile_n = wg / tiles_m;
+    return;
+  }
   constexpr int kXcds = 8;
   const int q = num_wg / kXcds, r = num_wg % kXcds;
   const int x = wg % kXcds, i = wg / kXcds;

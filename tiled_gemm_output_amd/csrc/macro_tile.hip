@@ -19,26 +19,41 @@ __device__ __forceinline__ void store_out(void* C, int64_t off, float x) {
 }
 
 // Each thread sums G consecutive elements of one row (G = 4 when N % 4 == 0: the
-// workspace is dense, so every group is a 16-byte aligned vector of one row).
-template <int OUT, int G>
+// workspace is dense, so every group is a 16-byte aligned vector of one row). VS:
+// C's rows start on a multiple of four elements and C is aligned to four elements, so
+// the four results go out in one store. The workspace is read once: non-temporal loads.
+template <int OUT, int G, bool VS>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* ws, int splits, void* C, int64_t ldc, int M,
                                                            int N) {
   const int64_t slice = (int64_t)M * N, groups = slice / G;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < groups; q += (int64_t)gridDim.x * blockDim.x) {
     const int64_t e = q * G, r = e / N, c = e - r * N;
     if constexpr (G == 4) {
-      f32x4 acc = *(const f32x4*)(ws + e);
+      f32x4 acc = __builtin_nontemporal_load((const f32x4*)(ws + e));
       for (int s = 1; s < splits; ++s) {
-        const f32x4 x = *(const f32x4*)(ws + s * slice + e);
+        const f32x4 x = __builtin_nontemporal_load((const f32x4*)(ws + s * slice + e));
         acc.x += x.x;
         acc.y += x.y;
         acc.z += x.z;
         acc.w += x.w;
       }
-      store_out<OUT>(C, r * ldc + c, acc.x);
-      store_out<OUT>(C, r * ldc + c + 1, acc.y);
-      store_out<OUT>(C, r * ldc + c + 2, acc.z);
-      store_out<OUT>(C, r * ldc + c + 3, acc.w);
+      if constexpr (VS) {
+        const int64_t off = r * ldc + c;
+        if constexpr (OUT == OUT_F32) {
+          *(f32x4*)((float*)C + off) = acc;
+        } else if constexpr (OUT == OUT_BF16) {
+          *(u32x2*)((uint16_t*)C + off) = u32x2{pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w)};
+        } else {
+          *(u32x2*)((uint16_t*)C + off) =
+              u32x2{(uint32_t)f32_to_f16_rne(acc.x) | ((uint32_t)f32_to_f16_rne(acc.y) << 16),
+                    (uint32_t)f32_to_f16_rne(acc.z) | ((uint32_t)f32_to_f16_rne(acc.w) << 16)};
+        }
+      } else {
+        store_out<OUT>(C, r * ldc + c, acc.x);
+        store_out<OUT>(C, r * ldc + c + 1, acc.y);
+        store_out<OUT>(C, r * ldc + c + 2, acc.z);
+        store_out<OUT>(C, r * ldc + c + 3, acc.w);
+      }
     } else {
       float acc = ws[e];
       for (int s = 1; s < splits; ++s) acc += ws[s * slice + e];
@@ -53,10 +68,17 @@ static void launch_reduce(const float* ws, int splits, void* C, int64_t ldc, int
   const int64_t groups = (int64_t)M * N / (v4 ? 4 : 1);
   int64_t blocks = (groups + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  if (v4)
-    hipLaunchKernelGGL((splitk_reduce_kernel<OUT, 4>), dim3((unsigned)blocks), dim3(256), 0, s, ws, splits, C, ldc, M, N);
+  const int64_t ob = OUT == OUT_F32 ? 4 : 2;
+  const bool vs = v4 && ldc % 4 == 0 && (uintptr_t)C % (uintptr_t)(4 * ob) == 0;
+  if (vs)
+    hipLaunchKernelGGL((splitk_reduce_kernel<OUT, 4, true>), dim3((unsigned)blocks), dim3(256), 0, s, ws, splits, C, ldc,
+                       M, N);
+  else if (v4)
+    hipLaunchKernelGGL((splitk_reduce_kernel<OUT, 4, false>), dim3((unsigned)blocks), dim3(256), 0, s, ws, splits, C,
+                       ldc, M, N);
   else
-    hipLaunchKernelGGL((splitk_reduce_kernel<OUT, 1>), dim3((unsigned)blocks), dim3(256), 0, s, ws, splits, C, ldc, M, N);
+    hipLaunchKernelGGL((splitk_reduce_kernel<OUT, 1, false>), dim3((unsigned)blocks), dim3(256), 0, s, ws, splits, C,
+                       ldc, M, N);
 }
 
 hipError_t launch_splitk_reduce(const float* ws, int splits, void* C, int64_t ldc, int M, int N, int out,
