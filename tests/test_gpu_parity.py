@@ -321,6 +321,37 @@ def test_automatic_split_of_one_round(h, o, shape, splits):
     sampled_check(h, o, a, b, tgemm.BF16_F32, rows, cols)
 
 
+@pytest.mark.parametrize("shape,tile,splits", [
+    ((128, 4096, 2048), (128, 128, 64), 0), ((4096, 128, 2048), (128, 128, 64), 0),
+    ((100, 3000, 1000), (128, 128, 64), 3), ((3000, 100, 1000), (128, 128, 64), 1),
+    ((64, 8192, 640), (64, 64, 64), 0), ((8192, 64, 640), (64, 64, 64), 2),
+    ((200, 5000, 1500), (256, 256, 64), 0), ((256, 3000, 700), (256, 128, 64), 0)], ids=str)
+def test_single_tile_row_or_column(h, o, shape, tile, splits):
+    """C covered by one row or one column of tiles: the workgroups keep the hardware's
+    order (no panel is shared, so nothing is grouped on an XCD), with and without
+    split-K. Every output against the oracle: integer-valued inputs bit for bit,
+    N(0, 1) inputs to the accuracy rule."""
+    M, N, K = shape
+    p = plan_of(h, M, N, K, tgemm.BF16_F32, splits=splits, tile=tile)
+    print("single tile row/column %s: tile %dx%d split %d grid %d" % (
+        shape, p["tile_m"], p["tile_n"], p["split_k"], p["grid"]), flush=True)
+    assert -(-M // p["tile_m"]) == 1 or -(-N // p["tile_n"]) == 1, p
+    for dtype, kind in [(tgemm.BF16_F32, "bf16"), (tgemm.F16_F16, "f16")]:
+        a = inputs.draw((M, K), "small_int", kind, 301)
+        b = inputs.draw((K, N), "small_int", kind, 302)
+        set_tile(h, tile)
+        tgemm.check(tgemm.gemm_set_split_k(h, splits), "gemm_set_split_k")
+        try:
+            c, dc = G.run(h, a, b, dtype)
+        finally:
+            set_tile(h, None)
+            tgemm.gemm_set_split_k(h, 0)
+        assert dc.untouched_outside(), "kernel wrote outside C"
+        assert np.array_equal(c, oracle_ref(o, a, b, dtype).view(G.np_int(tgemm.OUT_BYTES[dtype]))), (shape, dtype)
+        a, b = inputs.random_case(M, N, K, kind, seed=303)
+        check_full(h, o, a, b, dtype, tile=tile, splits=splits)
+
+
 @pytest.mark.parametrize("shape", [(2600, 1900, 8300), (1000, 1000, 42000)], ids=str)
 def test_automatic_split_of_few_256_tiles(h, o, shape):
     """At most 128 tiles of 256x256 with slices of at least 40 K-tiles: the automatic
