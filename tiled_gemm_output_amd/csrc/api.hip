@@ -763,7 +763,8 @@ gemm_status_t launch_mfma_part(WsSource& wsrc, const gemm_plan_t& p, int splits,
     e = tg::launch_macro(find_macro(p.tile_m, p.tile_n, p.tile_k, p.stages), w, in_kind(dtype), 0, p.vector_loads != 0,
                          s, grid, splits, ta, tb);
     if (e == hipSuccess)
-      e = tg::launch_splitk_reduce((const float*)ws, splits, C, ldc, (int)M, (int)N, out_kind(dtype), s);
+      e = tg::launch_splitk_reduce((const float*)ws, splits, C, ldc, (int)M, (int)N, out_kind(dtype),
+                                   tg::SplitTiles{p.tile_m, p.tile_n, a.tiles_m, a.tiles_n, a.group_m == 0}, s);
   }
   return e == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

@@ -35,9 +35,16 @@ extern const MacroShape kMacroShapes[kNumMacroShapes];
 // (K x M, row stride lda); tb: B is stored transposed (N x K, row stride ldb).
 hipError_t launch_macro(int shape, const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid,
                         int splits, bool ta, bool tb);
+// The C tiles of the split-K launch whose partials are summed: their size, count, and
+// whether the workgroups kept the hardware's order (MacroArgs::group_m == 0).
+struct SplitTiles {
+  int bm, bn, tiles_m, tiles_n;
+  bool hw_order;
+};
 // C[0:M, 0:N] = sum over s < splits of ws[s][M][N] (dense fp32 partials, summed in slice order),
 // rounded to the output format (out: 0 = f32, 1 = bf16, 2 = f16).
-hipError_t launch_splitk_reduce(const float* ws, int splits, void* C, int64_t ldc, int M, int N, int out, hipStream_t s);
+hipError_t launch_splitk_reduce(const float* ws, int splits, void* C, int64_t ldc, int M, int N, int out,
+                                const SplitTiles& g, hipStream_t s);
 hipError_t launch_small(const MacroArgs& a, int in, int out, bool vec, hipStream_t s, int64_t grid, bool ta, bool tb);
 
 struct I32Args {
