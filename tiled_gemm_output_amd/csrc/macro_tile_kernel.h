@@ -19,12 +19,11 @@
 //  * waves of 64 lanes, each owning a (BM/WM) x (BN/WN) sub-tile computed with
 //    v_mfma_f32_32x32x16_{bf16,f16};
 //  * a pipeline of LDS stages with one barrier per K-step: K-tile kt lives in A
-//    stage kt % NA and B stage kt % NB and is loaded D steps before it is
-//    multiplied (D = 2 with three A stages and two B stages by default; D = 3 with
-//    four of each for launches with at most one workgroup per compute unit, where
-//    more loads in flight hide memory latency that other workgroups cannot). A
-//    stage is only ever refilled once every wave's reads of it have completed
-//    (see the main loop);
+//    stage kt % NA and B stage kt % NB; A is loaded DA and B DB steps before the
+//    step that multiplies it (by default three A stages and two B stages, DA = 3 and
+//    DB = 2; four of each and DA = DB = 3 for launches with at most one workgroup
+//    per compute unit). A stage is only ever refilled once every wave's reads of it
+//    have completed (see the main loop);
 //  * vector path (A and B at even addresses: any shape and leading dimension):
 //    16-byte buffer loads straight from global memory into LDS (buffer_load_dwordx4
 //    ... lds), no register staging; out-of-range lanes use an offset beyond the
@@ -49,8 +48,9 @@ namespace tg {
 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
-// NS names the pipeline: 2 = K-tiles loaded two steps ahead into three A stages and
-// two B stages; 4 = loaded three steps ahead into four stages of each.
+// NS names the pipeline: 2 = three A stages, A loaded three steps ahead, and two B
+// stages, B loaded two steps ahead (three and three for a wave tile one MFMA block
+// high); 4 = four stages of each, loaded three steps ahead.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int NS_ = 2>
 struct MacroCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, NS = NS_;
@@ -60,22 +60,21 @@ struct MacroCfg {
   static constexpr int kFM = kWTM / 32, kFN = kWTN / 32;  // 32x32 MFMA blocks per wave
   static constexpr int kABytes = BM * BK * 2, kBBytes = BK * BN * 2;
   static constexpr int kSubsteps = BK / 16;
-  static constexpr int D = NS == 2 ? 2 : NS - 1;  // K-steps between a K-tile's load and its use
-  // The last substep's MFMAs are split around the step's barrier: block rows
-  // [0, kFM / 2) before it, the rest after. B's fragments are all consumed before
-  // the barrier when that first half is not empty (kFM >= 2).
-  static constexpr bool kBDoneAtBarrier = kFM >= 2;
-  static constexpr int NA = NS == 2 ? 3 : NS;                              // A stages
-  static constexpr int NB = NS == 2 ? (kBDoneAtBarrier ? 2 : 3) : NS;      // B stages
+  static constexpr int NA = NS == 2 ? 3 : NS;                 // A stages
+  static constexpr int NB = NS == 2 ? (kFM >= 2 ? 2 : 3) : NS;  // B stages
+  // K-steps between a K-tile's load (issued right after one step's barrier) and the
+  // step that multiplies it: every stage not holding a K-tile still to be multiplied.
+  static constexpr int DA = NS == 2 ? NA : NS - 1, DB = NS == 2 ? NB : NS - 1;
   static constexpr int L = NA / gcd_c(NA, NB) * NB;  // steps after which the stage pattern repeats
   static constexpr int kLds = NA * kABytes + NB * kBBytes;
   static_assert(BK == 64, "four 16-deep substeps per K-step");
   static_assert(NS == 2 || NS == 4, "two pipelines");
-  // The refill of K-tile st + D, issued right after step st's barrier, must not land
-  // in a stage that is still to be read: the stages of st + 1 .. st + D - 1, and the
-  // stage of st itself unless every wave consumed its last reads of it before the
-  // barrier (B when kBDoneAtBarrier; never A).
-  static_assert(D >= 2 && NA >= D + 1 && NB >= D + (kBDoneAtBarrier ? 0 : 1),
+  // Every wave has completed its LDS reads of K-tile st when it reaches step st's
+  // barrier, so the refill of K-tile st + DA (st + DB), issued right after it, may
+  // take the stage of st but none of st + 1 .. st + DA - 1 (DB - 1): NA >= DA, NB >= DB.
+  // B goes first in a batch of refills, at most one K-tile behind A (the waits count
+  // loads in issue order).
+  static_assert(DA >= 2 && DB >= 2 && NA >= DA && NB >= DB && (DA == DB || DA == DB + 1),
                 "refill targets a stage no wave still reads");
   static_assert(kFM >= 1 && kFN >= 1 && kWTM % 32 == 0 && kWTN % 32 == 0, "wave tile must be a multiple of 32x32");
   static_assert(kLds <= 160 * 1024, "LDS budget");
@@ -254,7 +253,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   constexpr int kAPer = OA::kPer, kBPer = OB::kPer;
   constexpr int NR = FM * OA::kReads + FN * OB::kReads;  // LDS reads per substep
   constexpr int NM = FM * FN;                            // MFMAs per substep
-  constexpr int NA = Cfg::NA, NB = Cfg::NB, D = Cfg::D, L = Cfg::L;
+  constexpr int NA = Cfg::NA, NB = Cfg::NB, DA = Cfg::DA, DB = Cfg::DB, L = Cfg::L;
   static_assert(VEC || Cfg::NS == 2, "the element loader stages one K-tile ahead in registers");
 
   const int tid = threadIdx.x;
@@ -318,17 +317,21 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   // zeros. With an odd stored row length (K for a K-contiguous operand, M or N
   // otherwise) the dword holding the matrix's last element also covers two bytes past
   // the end, so that element reads as zero too; it is written into LDS afterwards.
-  auto issue_loads = [&](TG_LDS char* sa, TG_LDS char* sb, int kt) __attribute__((always_inline)) {
+  auto issue_a = [&](TG_LDS char* sa, int kt) __attribute__((always_inline)) {
     const bool ok = (unsigned)kt < (unsigned)nk;
     const int k0 = ok ? (kt_base + kt) * BK : 0;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A + a_origin(k0), ok ? a_extent(k0) : 0);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + b_origin(k0), ok ? b_extent(k0) : 0);
 #pragma unroll
     for (int t = 0; t < kAPer; ++t) {
       uint32_t off = a_off[t];
       if constexpr (LOAD == kLoadVec) off = (k0 + OA::kpos(lwave, t, lane) < K) ? off : kOutOfRange;
       load_lds_x4(ra, sa + (lwave * kAPer + t) * 1024, off);
     }
+  };
+  auto issue_b = [&](TG_LDS char* sb, int kt) __attribute__((always_inline)) {
+    const bool ok = (unsigned)kt < (unsigned)nk;
+    const int k0 = ok ? (kt_base + kt) * BK : 0;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.B + b_origin(k0), ok ? b_extent(k0) : 0);
 #pragma unroll
     for (int t = 0; t < kBPer; ++t) {
       uint32_t off = b_off[t];
@@ -477,45 +480,57 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   // K-tile kt lives in A stage kt % NA and B stage kt % NB. Step st multiplies
   // K-tile st in four substeps; the reads of substep s+1 are issued among the MFMAs
   // of substep s. The step's barrier sits after the first half of the last
-  // substep's MFMAs: before it each loading wave waits until its loads of K-tile
-  // st + 1 have landed (those of K-tiles st + 2 .. st + D - 1 may still be in
-  // flight); right after it K-tile st + D is loaded and the first fragments of
-  // K-tile st + 1 are read, both covered by the second half of those MFMAs.
+  // substep's MFMAs: before it each wave waits until its own LDS reads have
+  // completed, and each loading wave until its loads of K-tile st + 1 have landed
+  // (later K-tiles may still be in flight); right after it the loading waves issue
+  // B's K-tile st + DB and A's K-tile st + DA, and every wave reads the first
+  // fragments of K-tile st + 1, all covered by the second half of those MFMAs.
   //
   // Why no stage is written while a wave may still read it ("Tiled Matrix
   // Multiplication", section 5: a barrier after the tile is consumed, before it
   // is overwritten). A wave's LDS read is complete once the wave has waited for
-  // its result (s_waitcnt lgkmcnt, which the compiler places before the MFMA
-  // that consumes it). Step st's reads of K-tile st end with the last substep's
-  // fragments, consumed by MFMAs before step st's barrier (B's, when kFM >= 2)
-  // or right after it, so before step st + 1's barrier. The refill of K-tile
-  // st + D is issued after step st's barrier into the stage that held K-tile
-  // st + D - NA (A) or st + D - NB (B): st - 1 or earlier (NA >= D + 1), all of
-  // whose reads every wave completed before step st's barrier; or, for B when
-  // kFM >= 2, possibly st itself (NB >= D), whose B reads are also complete
-  // before that barrier. The writes before step st's barrier (the element
-  // loader's K-tile st + 1, the clean-up of a last K-tile) go to the stages of
-  // K-tile st + 1, which held K-tile st + 1 - NA <= st - 2 (A) and st + 1 - NB
-  // (B: st - 2, or st - 1 when kFM >= 2), whose reads every wave completed before
-  // step st - 1's barrier, which every wave has passed. (The fragments read after
-  // the last step, from the stage of a K-tile past the slice, are never
-  // multiplied.)
+  // it (s_waitcnt lgkmcnt). Every read of K-tile st is issued before step st's
+  // barrier (the last substep's fragments are read during the third substep's
+  // MFMAs), and every wave waits for all its reads (lgkmcnt(0)) before that
+  // barrier, so once a wave has passed it no wave reads K-tile st or an earlier one
+  // any more. The refills issued right after step st's barrier go to the stages that
+  // held K-tile st + DA - NA (A) and st + DB - NB (B): st or earlier, since
+  // NA >= DA and NB >= DB. The writes before step st's barrier (the element loader's
+  // K-tile st + 1, the clean-up of a last K-tile) go to the stages of K-tile st + 1,
+  // which held K-tile st + 1 - NA and st + 1 - NB, at most st - 1, whose reads every
+  // wave completed before step st - 1's barrier. (The fragments read after the last
+  // step, from the stage of a K-tile past the slice, are never multiplied.)
+  //
+  // Loads complete in the order they are issued (a wave's s_waitcnt vmcnt counts
+  // the loads still in flight), so each batch of refills issues B before A. With
+  // DA == DB a batch holds one K-tile, and K-tile st + 1 is complete once at most
+  // DA - 2 batches are in flight. With DA = DB + 1, B's K-tile st + 1 is in batch
+  // st + 1 - DB behind the K-tile of A it needs (batch st - DB); only the A part of
+  // that batch and the DB - 2 batches after it may still be in flight.
   //
   // The stage pattern repeats every L steps: the loop body is one cycle of L
   // unrolled steps (stage indices are compile-time, so the compiler tracks the
   // direct loads of each stage apart), and the last nk % L steps follow it.
   constexpr int PER = kAPer + kBPer;  // direct loads per wave and K-tile
+  // loads a loading wave may leave in flight once K-tile 0 (k0) or K-tile st + 1 (k1) is complete
+  constexpr int kInFlight0 = DA == DB ? PER * (DA - 1) : kAPer + PER * (DB - 1);
+  constexpr int kInFlight1 = DA == DB ? PER * (DA - 2) : kAPer + PER * (DB - 2);
   i32x4 fa[FM], fb[FN], ga[FM], gb[FN];
   // The pipeline, for a wave that loads (LOADER) or one that only multiplies; the
   // two are separate branch-free copies, so the compiler tracks each one's loads
-  // exactly. A multiplying wave waits for nothing but the barriers: each loading
-  // wave has waited for its own loads of a K-tile before it arrives there.
+  // exactly. A multiplying wave waits for nothing but its reads and the barriers:
+  // each loading wave has waited for its own loads of a K-tile before it arrives there.
   auto run = [&](auto ROLE) __attribute__((always_inline)) {
     constexpr bool LOADER = decltype(ROLE)::value != 0;
     if constexpr (VEC) {
       if constexpr (LOADER) {
-        static_for<0, D>([&](auto i) { issue_loads(pA[i.value % NA], pB[i.value % NB], i.value); });
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (D - 1)));  // K-tile 0 landed
+        // the batches of steps -DA .. -1 in the steady order: B's K-tile b + DB, then A's b + DA
+        static_for<0, DA>([&](auto i) {
+          constexpr int b = i.value - DA;
+          if constexpr (b + DB >= 0) issue_b(pB[(b + DB) % NB], b + DB);
+          issue_a(pA[(b + DA) % NA], b + DA);
+        });
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kInFlight0));  // K-tile 0 landed
         fix_last(pA[0], pB[0], 0);
       }
     } else {
@@ -547,22 +562,26 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
       __builtin_amdgcn_sched_barrier(0);
       mfma_rows(ga, gb, 0, FM / 2);
       __builtin_amdgcn_sched_barrier(0);
-      // K-tile st + 1 must be complete in every wave before anyone reads it.
+      // K-tile st + 1 must be complete in every wave before anyone reads it, and no
+      // read of K-tile st may be in flight in any wave once the barrier is passed.
       if constexpr (VEC) {
         if constexpr (LOADER) {
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER * (D - 2)));  // its loads of K-tile st + 1 landed
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kInFlight1));  // its loads of K-tile st + 1 landed
           fix_last(na, nb, st + 1);
         }
       } else {
-        store_regs(na, nb);                  // K-tile st + 1, fetched one step ago
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        store_regs(na, nb);  // K-tile st + 1, fetched one step ago
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads and writes are done
       barrier_nofence();
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (VEC && LOADER)
-        issue_loads(pA[(j + D) % NA], pB[(j + D) % NB], st + D);  // past the last K-tile: zero-length, no traffic
-      else if constexpr (!VEC)
+      if constexpr (VEC && LOADER) {
+        // past the last K-tile: zero-length, no traffic
+        issue_b(pB[(j + DB) % NB], st + DB);
+        issue_a(pA[(j + DA) % NA], st + DA);
+      } else if constexpr (!VEC) {
         fetch_regs(st + 2);
+      }
       read_frags(na, nb, 0, fa, fb);
       mfma_rows(ga, gb, FM / 2, FM);
       interleave<(FM - FM / 2) * FN, NR, (VEC && LOADER) ? PER : 0>();
