@@ -34,6 +34,12 @@ CHOICES = [
     ((1337, 272, 3365), (64, 64, 2, 4, 0)),          # 33 tiles over 53 K-tiles: 16.6 (17.6 as 128x128 in 6)
     ((633, 542, 3251), (64, 64, 2, 4, 0)),           # 16.5 (18.2 as 128x128 in 6)
     ((512, 512, 8192), (64, 64, 4, 4, 0)),           # 16 tiles: 18.1 (20.2 as 128x128 in 12)
+    ((2048, 4096, 2048), (256, 128, 1, 2, 0)),       # one round of 256x128: 35.7 (37.7 as 128x128, two per CU)
+    ((768, 7936, 4096), (256, 128, 1, 2, 0)),        # 52.9 (58.3 as 128x128)
+    ((2560, 2560, 4096), (256, 128, 1, 2, 0)),       # 56.2 (61.0 as 128x128, 74.6 as 256x256)
+    ((3072, 3072, 8192), (256, 256, 1, 2, 0)),       # 144 tiles: 143.2 (176.3 as 128x128, 195.8 as 256x128)
+    ((3584, 3584, 4096), (256, 256, 1, 2, 0)),       # 196 tiles: 88.8 (106.1 as 256x128)
+    ((1536, 1536, 2048), (128, 128, 1, 4, 0)),       # 21.4 (26.0 as 256x128, 24.5 as 64x64)
 ]
 
 

@@ -245,8 +245,11 @@ int find_macro(int tm, int tn, int tk, int stages = 2) {
 // units), the 256x256 tile, which requests the fewest bytes per flop. Otherwise the
 // tile among 256x256, 256x128 and 128x128 with the lowest estimated time: rounds of
 // workgroups x per-CU work per round x the tile's measured cost per unit of work
-// relative to 256x256 (MI355X, bf16: 256x128 1.52; 128x128 1.28 with two workgroups
-// per CU, 1.86 with one). Tile counts that leave a nearly empty last round lose
+// relative to 256x256 (MI355X, bf16: 256x128 1.25; 128x128 1.28 with two workgroups
+// per CU, 1.86 with one; with A loaded three K-steps ahead, one round of 256x128 beat
+// two workgroups of 128x128 per CU by 4-10% on all 18 sampled shapes where a factor
+// of 1.52 had picked 128x128, e.g. 2048x4096x2048 35.7 against 37.7 us, 768x7936x4096
+// 52.9 against 58.3). Tile counts that leave a nearly empty last round lose
 // (3072^3: 144 tiles of 256x256 in one round beat 288 of 256x128 in two). Outputs
 // where 128x128 leaves at least half of the chip idle use 64x64: below 128 such tiles
 // when K is short (no split-K follows; 1024^3 runs in half the time on 64x64); below
@@ -277,7 +280,7 @@ int auto_macro(int64_t M, int64_t N, int64_t K) {
     int shape, bm, bn, occ;  // occ: workgroups that fit on one CU
     double f1, f2;           // relative cost per unit of work with 1 and with 2+ workgroups per CU
   };
-  const Cand cands[] = {{0, 256, 256, 1, 1.0, 1.0}, {1, 256, 128, 1, 1.52, 1.52}, {2, 128, 128, 2, 1.86, 1.28}};
+  const Cand cands[] = {{0, 256, 256, 1, 1.0, 1.0}, {1, 256, 128, 1, 1.25, 1.25}, {2, 128, 128, 2, 1.86, 1.28}};
   int best = 0;
   double best_t = 0.0;
   for (const Cand& c : cands) {
