@@ -163,7 +163,8 @@ def test_plan_tile_by_rounds_of_workgroups():
     assert tile(3072, 3072, 3072) == (256, 256, 1, 2)   # 144 tiles in one round, not 288 of 256x128 in two
     assert tile(3584, 3584, 3584) == (256, 256, 1, 2)   # 196 tiles
     assert tile(3072, 4096, 1024) == (256, 256, 1, 2)
-    assert tile(2560, 2560, 2560)[:2] == (128, 128)     # 100 of 256x256 would leave 156 CUs idle
+    assert tile(2560, 2560, 2560)[:2] == (256, 128)     # 100 of 256x256 would leave 156 CUs idle; 200 of 256x128
+    assert tile(2048, 4096, 2048)[:2] == (256, 128)     # one full round of 256x128, not 512 of 128x128
     assert tile(1024, 1024, 1024) == (64, 64, 1, 4)     # short K: 256 tiles of 64x64, 16 K-tiles each
     assert tile(512, 512, 512) == (64, 64, 1, 4)        # 8 K-tiles
     assert tile(1536, 1536, 1536)[:2] == (128, 128)     # 144 tiles of 128x128
