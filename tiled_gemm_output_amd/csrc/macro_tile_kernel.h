@@ -20,8 +20,8 @@
 //    v_mfma_f32_32x32x16_{bf16,f16};
 //  * a pipeline of LDS stages with one barrier per K-step: K-tile kt lives in A
 //    stage kt % NA and B stage kt % NB; A is loaded DA and B DB steps before the
-//    step that multiplies it (by default three A stages and two B stages, DA = 3 and
-//    DB = 2; four of each and DA = DB = 3 for launches with at most one workgroup
+//    step that multiplies it (by default two A stages and three B stages, DA = 2 and
+//    DB = 3; four of each and DA = DB = 3 for launches with at most one workgroup
 //    per compute unit). A stage is only ever refilled once every wave's reads of it
 //    have completed (see the main loop);
 //  * vector path (A and B at even addresses: any shape and leading dimension):
@@ -48,8 +48,8 @@ namespace tg {
 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
-// NS names the pipeline: 2 = three A stages, A loaded three steps ahead, and two B
-// stages, B loaded two steps ahead (three and three for a wave tile one MFMA block
+// NS names the pipeline: 2 = two A stages, A loaded two steps ahead, and three B
+// stages, B loaded three steps ahead (three and three for a wave tile one MFMA block
 // high); 4 = four stages of each, loaded three steps ahead.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int NS_ = 2>
 struct MacroCfg {
@@ -60,11 +60,11 @@ struct MacroCfg {
   static constexpr int kFM = kWTM / 32, kFN = kWTN / 32;  // 32x32 MFMA blocks per wave
   static constexpr int kABytes = BM * BK * 2, kBBytes = BK * BN * 2;
   static constexpr int kSubsteps = BK / 16;
-  static constexpr int NA = NS == 2 ? 3 : NS;                 // A stages
-  static constexpr int NB = NS == 2 ? (kFM >= 2 ? 2 : 3) : NS;  // B stages
+  static constexpr int NA = NS == 2 ? (kFM >= 2 ? 2 : 3) : NS;  // A stages
+  static constexpr int NB = NS == 2 ? 3 : NS;                   // B stages
   // K-steps between a K-tile's load (issued right after one step's barrier) and the
   // step that multiplies it: every stage not holding a K-tile still to be multiplied.
-  static constexpr int DA = NS == 2 ? NA : NS - 1, DB = NS == 2 ? NB : NS - 1;
+  static constexpr int DA = NS == 4 ? NS - 1 : NA, DB = NS == 4 ? NS - 1 : NB;
   static constexpr int L = NA / gcd_c(NA, NB) * NB;  // steps after which the stage pattern repeats
   static constexpr int kLds = NA * kABytes + NB * kBBytes;
   static_assert(BK == 64, "four 16-deep substeps per K-step");
@@ -72,9 +72,9 @@ struct MacroCfg {
   // Every wave has completed its LDS reads of K-tile st when it reaches step st's
   // barrier, so the refill of K-tile st + DA (st + DB), issued right after it, may
   // take the stage of st but none of st + 1 .. st + DA - 1 (DB - 1): NA >= DA, NB >= DB.
-  // B goes first in a batch of refills, at most one K-tile behind A (the waits count
-  // loads in issue order).
-  static_assert(DA >= 2 && DB >= 2 && NA >= DA && NB >= DB && (DA == DB || DA == DB + 1),
+  // In a batch of refills the operand loaded fewer steps ahead goes first, at most
+  // one K-tile behind the other (the waits count loads in issue order).
+  static_assert(DA >= 2 && DB >= 2 && NA >= DA && NB >= DB && DA - DB <= 1 && DB - DA <= 1,
                 "refill targets a stage no wave still reads");
   static_assert(kFM >= 1 && kFN >= 1 && kWTM % 32 == 0 && kWTN % 32 == 0, "wave tile must be a multiple of 32x32");
   static_assert(kLds <= 160 * 1024, "LDS budget");
@@ -502,19 +502,36 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   // step, from the stage of a K-tile past the slice, are never multiplied.)
   //
   // Loads complete in the order they are issued (a wave's s_waitcnt vmcnt counts
-  // the loads still in flight), so each batch of refills issues B before A. With
-  // DA == DB a batch holds one K-tile, and K-tile st + 1 is complete once at most
-  // DA - 2 batches are in flight. With DA = DB + 1, B's K-tile st + 1 is in batch
-  // st + 1 - DB behind the K-tile of A it needs (batch st - DB); only the A part of
-  // that batch and the DB - 2 batches after it may still be in flight.
+  // the loads still in flight), so each batch of refills issues first the operand
+  // loaded fewer steps ahead (B when DA = DB + 1, A when DB = DA + 1). With DA == DB a
+  // batch holds one K-tile, and K-tile st + 1 is complete once at most DA - 2 batches
+  // are in flight. With DA = DB + 1, B's K-tile st + 1 is in batch st + 1 - DB behind
+  // the K-tile of A it needs (batch st - DB); only the A part of that batch and the
+  // DB - 2 batches after it may still be in flight (and the same with A and B swapped).
   //
   // The stage pattern repeats every L steps: the loop body is one cycle of L
   // unrolled steps (stage indices are compile-time, so the compiler tracks the
   // direct loads of each stage apart), and the last nk % L steps follow it.
   constexpr int PER = kAPer + kBPer;  // direct loads per wave and K-tile
   // loads a loading wave may leave in flight once K-tile 0 (k0) or K-tile st + 1 (k1) is complete
-  constexpr int kInFlight0 = DA == DB ? PER * (DA - 1) : kAPer + PER * (DB - 1);
-  constexpr int kInFlight1 = DA == DB ? PER * (DA - 2) : kAPer + PER * (DB - 2);
+  constexpr int kDS = DA < DB ? DA : DB;                           // the shorter distance
+  constexpr int kLate = DA > DB ? kAPer : (DB > DA ? kBPer : 0);    // loads of the longer one per batch
+  constexpr int kInFlight0 = DA == DB ? PER * (DA - 1) : kLate + PER * (kDS - 1);
+  constexpr int kInFlight1 = DA == DB ? PER * (DA - 2) : kLate + PER * (kDS - 2);
+  // The batch of refills issued right after step j's barrier (j < 0: the prologue's
+  // batches; st = j there): A's K-tile st + DA and B's st + DB, the operand loaded
+  // fewer steps ahead first; in the prologue K-tiles before 0 are skipped.
+  auto refill = [&](auto J, int st) __attribute__((always_inline)) {
+    constexpr int j = decltype(J)::value;
+    constexpr int ia = ((j + DA) % NA + NA) % NA, ib = ((j + DB) % NB + NB) % NB;
+    if constexpr (DB > DA) {
+      if constexpr (j + DA >= 0) issue_a(pA[ia], st + DA);
+      issue_b(pB[ib], st + DB);
+    } else {
+      if constexpr (j + DB >= 0) issue_b(pB[ib], st + DB);
+      issue_a(pA[ia], st + DA);
+    }
+  };
   i32x4 fa[FM], fb[FN], ga[FM], gb[FN];
   // The pipeline, for a wave that loads (LOADER) or one that only multiplies; the
   // two are separate branch-free copies, so the compiler tracks each one's loads
@@ -524,11 +541,11 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
     constexpr bool LOADER = decltype(ROLE)::value != 0;
     if constexpr (VEC) {
       if constexpr (LOADER) {
-        // the batches of steps -DA .. -1 in the steady order: B's K-tile b + DB, then A's b + DA
-        static_for<0, DA>([&](auto i) {
-          constexpr int b = i.value - DA;
-          if constexpr (b + DB >= 0) issue_b(pB[(b + DB) % NB], b + DB);
-          issue_a(pA[(b + DA) % NA], b + DA);
+        // the batches of steps -max(DA, DB) .. -1 in the steady order
+        constexpr int kDL = DA > DB ? DA : DB;
+        static_for<0, kDL>([&](auto i) {
+          constexpr int b = i.value - kDL;
+          refill(IC<b>{}, b);
         });
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kInFlight0));  // K-tile 0 landed
         fix_last(pA[0], pB[0], 0);
@@ -576,9 +593,7 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
       barrier_nofence();
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (VEC && LOADER) {
-        // past the last K-tile: zero-length, no traffic
-        issue_b(pB[(j + DB) % NB], st + DB);
-        issue_a(pA[(j + DA) % NA], st + DA);
+        refill(J, st);  // past the last K-tile: zero-length, no traffic
       } else if constexpr (!VEC) {
         fetch_regs(st + 2);
       }
