@@ -192,17 +192,21 @@ def test_plan_split_k():
 
 def test_plan_stages():
     """The deep pipeline (4 stages of each operand) when the launch has at most one
-    workgroup per compute unit (256) and every K-slice has at least 8 K-tiles; the
-    default one (3 A stages, 2 B stages) otherwise."""
+    workgroup per compute unit (256) and every K-slice has at least 8 K-tiles, except
+    for unsplit 128x128 tiles; the default one (2 A stages, 3 B stages; 3 and 3 for
+    the 64x64 tile) otherwise."""
     assert plan(8192, 8192, 8192, tgemm.BF16_BF16)["stages"] == 2             # 1024 workgroups
     p = plan(128, 8192, 8192, tgemm.BF16_F32)                                  # 64 tiles x 4 slices of 32 K-tiles
     assert (p["grid"] * p["split_k"], p["stages"]) == (256, 4)
-    p = plan(1792, 1792, 1096, tgemm.BF16_BF16)                                # 196 tiles, 18 K-tiles (ragged K)
-    assert (p["tile_m"], p["grid"], p["split_k"], p["stages"]) == (128, 196, 1, 4)
-    assert plan(1792, 1792, 900, tgemm.BF16_BF16)["stages"] == 4              # 15 K-tiles
-    assert plan(1792, 1792, 448, tgemm.BF16_BF16)["stages"] == 2              # 7 K-tiles: too short
-    assert plan(1792, 1794, 1096, tgemm.BF16_BF16)["stages"] == 4             # odd N: still direct loads
-    assert plan(1792, 1792, 1096, tgemm.BF16_BF16, A=0x10001)["stages"] == 2  # odd address: element loader
+    p = plan(768, 768, 8192, tgemm.BF16_BF16)                                  # 36 tiles of 128x128 x 7 slices
+    assert (p["tile_m"], p["grid"] * p["split_k"], p["stages"]) == (128, 252, 4)
+    p = plan(1792, 1792, 1096, tgemm.BF16_BF16)                                # 196 unsplit tiles of 128x128
+    assert (p["tile_m"], p["grid"], p["split_k"], p["stages"]) == (128, 196, 1, 2)
+    p = plan(1024, 1024, 1096, tgemm.BF16_BF16)                                # 256 tiles of 64x64, 18 K-tiles (ragged K)
+    assert (p["tile_m"], p["grid"], p["split_k"], p["stages"]) == (64, 256, 1, 4)
+    assert plan(1024, 1024, 900, tgemm.BF16_BF16)["stages"] == 4              # 15 K-tiles
+    assert plan(1024, 1024, 448, tgemm.BF16_BF16)["stages"] == 2              # 7 K-tiles: too short
+    assert plan(1024, 1024, 1096, tgemm.BF16_BF16, A=0x10001)["stages"] == 2  # odd address: element loader
     assert plan(9, 9, 9, tgemm.I32_I32)["stages"] == 1
     assert plan(0, 9, 9, tgemm.BF16_F32)["stages"] == 0
 

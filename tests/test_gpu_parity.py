@@ -423,14 +423,14 @@ def test_split_k_setting_limits(h, o):
 
 # ---------------------------------------------------------------- 4-stage pipeline
 
-DEEP = [(1792, 1792, 1096), (1000, 1000, 4096), (136, 2056, 4096), (200, 968, 8000)]
+DEEP = [(1100, 1000, 6000), (1000, 1000, 1096), (1000, 1000, 4096), (136, 2056, 4096), (200, 968, 8000)]
 
 
 @pytest.mark.parametrize("shape", DEEP, ids=str)
 def test_deep_pipeline(h, o, shape):
     """Launches of at most one workgroup per compute unit run the 4-stage twin of
-    the tile (K-tile counts that are not a multiple of the 4-step stage cycle,
-    ragged K tails, edge tiles, split-K): random inputs to the accuracy rule,
+    the tile (64x64, or 128x128 cut into K-slices; K-tile counts that are not a
+    multiple of the 4-step stage cycle, ragged K tails, edge tiles): random inputs to the accuracy rule,
     integer-valued inputs bit for bit, in every format and in the transposed forms."""
     M, N, K = shape
     for n, dtype in enumerate([tgemm.BF16_BF16, tgemm.F16_F32, tgemm.BF16_F32, tgemm.F16_F16]):
@@ -448,12 +448,15 @@ def test_deep_pipeline(h, o, shape):
 
 
 def test_deep_pipeline_forced_tile(h, o):
-    """A forced 128x128 or 64x64 tile also gets the 4-stage pipeline when the launch is small."""
-    for tile in [(128, 128, 64), (64, 64, 64)]:
-        p = plan_of(h, 520, 264, 2000, tgemm.BF16_F32, tile=tile)
+    """A forced 64x64 tile, or a forced 128x128 tile cut into K-slices, also gets the
+    4-stage pipeline when the launch is small (an unsplit 128x128 tile keeps two A
+    stages and three B stages)."""
+    for tile, splits in [((128, 128, 64), 2), ((64, 64, 64), 0)]:
+        p = plan_of(h, 520, 264, 2000, tgemm.BF16_F32, splits=splits, tile=tile)
         assert p["stages"] == 4 and (p["tile_m"], p["tile_n"]) == tile[:2]
         a, b = inputs.random_case(520, 264, 2000, "bf16", seed=tile[0])
-        check_full(h, o, a, b, tgemm.BF16_F32, tile=tile)
+        check_full(h, o, a, b, tgemm.BF16_F32, tile=tile, splits=splits)
+    assert plan_of(h, 520, 264, 2000, tgemm.BF16_F32, tile=(128, 128, 64))["stages"] == 2
 
 
 # ---------------------------------------------------------------- output rounding edge cases
@@ -633,24 +636,27 @@ def test_k_step_counts(h, o, tile):
 @pytest.mark.parametrize("tile", [(64, 64, 64), (128, 128, 64)], ids=str)
 def test_k_step_counts_four_stages(h, o, tile):
     """The 4-stage twins (launches of at most 256 workgroups with at least 8 K-tiles per
-    slice): K-tile counts from the threshold up, every remainder of the 4-step stage
-    cycle, exact against the oracle."""
+    slice; the 128x128 tile cut into two K-slices): K-tile counts per slice from the
+    threshold up, every remainder of the 4-step stage cycle, exact against the oracle."""
     tm, tn, tk = tile
     M, N = 2 * tm + 3, 3 * tn - 7
+    splits = 2 if tm == 128 else 0
     seen = set()
     for nk in (8, 9, 10, 11, 12, 16, 17, 18, 19):
-        for K in (tk * nk, tk * nk - 5):
+        for K in (tk * nk * max(splits, 1), tk * nk * max(splits, 1) - 5):
             a = inputs.draw((M, K), "small_int", "f16", 300 + K)
             b = inputs.draw((K, N), "small_int", "f16", 400 + K)
             ref = oracle_ref(o, a, b, tgemm.F16_F32).view(np.int32)
             set_tile(h, tile)
+            tgemm.check(tgemm.gemm_set_split_k(h, splits), "gemm_set_split_k")
             try:
                 p = tgemm.gemm_plan(h, M, N, K, 1 << 20, K, 1 << 30, N, 1 << 34, N, tgemm.F16_F32)
                 seen.add(p["stages"])
-                print("4-stage k-steps tile %s K %d stages %d" % (tile, K, p["stages"]), flush=True)
+                print("4-stage k-steps tile %s K %d splits %d stages %d" % (tile, K, splits, p["stages"]), flush=True)
                 c, _ = G.run(h, a, b, tgemm.F16_F32)
             finally:
                 set_tile(h, None)
+                tgemm.gemm_set_split_k(h, 0)
             assert np.array_equal(c, ref), (tile, K, p["stages"])
     assert 4 in seen, seen
 

@@ -129,8 +129,8 @@ def test_ragged_direct_loads_split_k(h, o, ops, splits):
 
 
 def test_ragged_direct_loads_four_stages(h, o):
-    """The 4-stage pipeline (a single round of workgroups, long K) on ragged extents."""
-    for (M, N, K), ops in [((1792, 1794, 1096), (N_, N_)), ((1791, 1793, 1097), (T_, T_))]:
+    """The 4-stage pipeline (a single round of workgroups in K-slices, long K) on ragged extents."""
+    for (M, N, K), ops in [((1100, 1002, 6000), (N_, N_)), ((1099, 1001, 6001), (T_, T_))]:
         (ra, la), (rb, lb) = stored(M, N, K, ops)
         p = plan(h, M, N, K, ops, la, lb, N, (0, 0, 0), tgemm.BF16_BF16)
         assert p["stages"] == 4, p

@@ -18,7 +18,7 @@ CHOICES = [
     ((1536, 1536, 8192), (128, 128, 3, 2, 0)),       # 144 tiles: 53.3 (64.2 with 2 slices)
     ((1280, 1280, 8192), (128, 128, 5, 2, 0)),       # 41.4 (47.9 with 2)
     ((2048, 2048, 8192), (128, 128, 2, 2, 0)),       # 75.4 (81.9 unsplit)
-    ((2048, 2048, 4096), (128, 128, 1, 4, 0)),       # 40.1 (46.0 with 2)
+    ((2048, 2048, 4096), (128, 128, 1, 2, 0)),       # 40.8 (44.3 with 4 stages, 46.0 in 2 slices)
     ((6713, 307, 3517), (128, 128, 3, 2, 0)),        # 43.3 (49.8 unsplit)
     ((768, 768, 8192), (128, 128, 7, 4, 0)),         # 24.0 (44.8 as 144 unsplit 64x64 tiles)
     ((768, 768, 2048), (64, 64, 1, 4, 0)),           # 13.5 (17.1 as 128x128 split)
@@ -39,7 +39,7 @@ CHOICES = [
     ((2560, 2560, 4096), (256, 128, 1, 2, 0)),       # 56.2 (61.0 as 128x128, 74.6 as 256x256)
     ((3072, 3072, 8192), (256, 256, 1, 2, 0)),       # 144 tiles: 143.2 (176.3 as 128x128, 195.8 as 256x128)
     ((3584, 3584, 4096), (256, 256, 1, 2, 0)),       # 196 tiles: 88.8 (106.1 as 256x128)
-    ((1536, 1536, 2048), (128, 128, 1, 4, 0)),       # 21.4 (26.0 as 256x128, 24.5 as 64x64)
+    ((1536, 1536, 2048), (128, 128, 1, 2, 0)),       # 20.3 (21.0 with 4 stages, 26.0 as 256x128, 24.5 as 64x64)
 ]
 
 

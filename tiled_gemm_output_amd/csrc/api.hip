@@ -544,9 +544,14 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
     // Deeper pipeline: when the launch leaves at most one workgroup per compute unit
     // (so no other workgroup hides a workgroup's memory latency) and each K-slice is
     // at least kDeepMinKTiles long, the 4-stage twin of the tile keeps three K-tiles of
-    // loads in flight.
+    // both operands in flight. Not for unsplit 128x128 tiles, where two A stages and
+    // three B stages do better (MI355X, bf16: 2048x2048x4096 40.8 against 44.3 us,
+    // 1536x1536x2048 20.3 against 21.0; split, the twin keeps a small lead: 128x8192x8192
+    // in 4 slices 31.0 against 31.5).
     const int64_t nk_slice = cdiv(nk, p.split_k);
-    if (p.kernel == 4 && p.vector_loads && p.grid * p.split_k <= kDeepMaxWorkgroups && nk_slice >= kDeepMinKTiles) {
+    const bool unsplit128 = p.tile_m == 128 && p.tile_n == 128 && p.split_k == 1;
+    if (p.kernel == 4 && p.vector_loads && p.grid * p.split_k <= kDeepMaxWorkgroups && nk_slice >= kDeepMinKTiles &&
+        !unsplit128) {
       const int deep = find_macro(p.tile_m, p.tile_n, p.tile_k, 4);
       if (deep >= 0) {
         p.stages = 4;
