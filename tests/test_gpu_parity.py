@@ -352,6 +352,29 @@ def test_single_tile_row_or_column(h, o, shape, tile, splits):
         check_full(h, o, a, b, dtype, tile=tile, splits=splits)
 
 
+@pytest.mark.parametrize("ldc_pad,c_off", [(0, 0), (1, 0), (4, 1), (3, 2)], ids=str)
+def test_split_reduction_per_tile_layouts(h, o, ldc_pad, c_off):
+    """The per-tile split-K reduction (one row of 128x128 tiles, a multiple of 8 of them,
+    in the hardware's order) with C rows padded and C offset from its allocation, so
+    that some rows or the base leave the four-element alignment of its vector stores:
+    every output format, integer-valued inputs, bit for bit against the oracle."""
+    M, N, K = 128, 2048, 3000
+    p = plan_of(h, M, N, K, tgemm.BF16_F32, splits=3, tile=(128, 128, 64))
+    assert (p["grid"], p["split_k"]) == (16, 3), p
+    for dtype, kind in [(tgemm.BF16_F32, "bf16"), (tgemm.BF16_BF16, "bf16"), (tgemm.F16_F16, "f16"), (tgemm.F16_F32, "f16")]:
+        a = inputs.draw((M, K), "small_int", kind, 501)
+        b = inputs.draw((K, N), "small_int", kind, 502)
+        set_tile(h, (128, 128, 64))
+        tgemm.check(tgemm.gemm_set_split_k(h, 3), "gemm_set_split_k")
+        try:
+            c, dc = G.run(h, a, b, dtype, ldc=N + ldc_pad, offs=(0, 0, c_off))
+        finally:
+            set_tile(h, None)
+            tgemm.gemm_set_split_k(h, 0)
+        assert dc.untouched_outside(), "kernel wrote outside C"
+        assert np.array_equal(c, oracle_ref(o, a, b, dtype).view(G.np_int(tgemm.OUT_BYTES[dtype]))), (dtype, ldc_pad, c_off)
+
+
 @pytest.mark.parametrize("shape", [(2600, 1900, 8300), (1000, 1000, 42000)], ids=str)
 def test_automatic_split_of_few_256_tiles(h, o, shape):
     """At most 128 tiles of 256x256 with slices of at least 40 K-tiles: the automatic
