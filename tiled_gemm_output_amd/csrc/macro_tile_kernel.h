@@ -503,11 +503,12 @@ __global__ __launch_bounds__(Cfg::kThreads, 1) void macro_tile_kernel(MacroArgs 
   //
   // Loads complete in the order they are issued (a wave's s_waitcnt vmcnt counts
   // the loads still in flight), so each batch of refills issues first the operand
-  // loaded fewer steps ahead (B when DA = DB + 1, A when DB = DA + 1). With DA == DB a
+  // loaded fewer steps ahead (A when DB = DA + 1, B when DA = DB + 1). With DA == DB a
   // batch holds one K-tile, and K-tile st + 1 is complete once at most DA - 2 batches
-  // are in flight. With DA = DB + 1, B's K-tile st + 1 is in batch st + 1 - DB behind
-  // the K-tile of A it needs (batch st - DB); only the A part of that batch and the
-  // DB - 2 batches after it may still be in flight (and the same with A and B swapped).
+  // are in flight. With DB = DA + 1, A's part of K-tile st + 1 comes first in batch
+  // st + 1 - DA, the later of the two batches that hold K-tile st + 1 (B's part is in
+  // batch st - DA); only the B part of that batch and the DA - 2 batches after it may
+  // still be in flight (and the same with A and B swapped when DA = DB + 1).
   //
   // The stage pattern repeats every L steps: the loop body is one cycle of L
   // unrolled steps (stage indices are compile-time, so the compiler tracks the
