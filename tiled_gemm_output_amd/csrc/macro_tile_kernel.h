@@ -49,8 +49,7 @@ namespace tg {
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
 // NS names the pipeline: 2 = two A stages, A loaded two steps ahead, and three B
-// stages, B loaded three steps ahead (three and three for a wave tile one MFMA block
-// high); 4 = four stages of each, loaded three steps ahead.
+// stages, B loaded three steps ahead; 4 = four stages of each, loaded three steps ahead.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int NS_ = 2>
 struct MacroCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, NS = NS_;
@@ -60,8 +59,8 @@ struct MacroCfg {
   static constexpr int kFM = kWTM / 32, kFN = kWTN / 32;  // 32x32 MFMA blocks per wave
   static constexpr int kABytes = BM * BK * 2, kBBytes = BK * BN * 2;
   static constexpr int kSubsteps = BK / 16;
-  static constexpr int NA = NS == 2 ? (kFM >= 2 ? 2 : 3) : NS;  // A stages
-  static constexpr int NB = NS == 2 ? 3 : NS;                   // B stages
+  static constexpr int NA = NS == 2 ? 2 : NS;  // A stages
+  static constexpr int NB = NS == 2 ? 3 : NS;  // B stages
   // K-steps between a K-tile's load (issued right after one step's barrier) and the
   // step that multiplies it: every stage not holding a K-tile still to be multiplied.
   static constexpr int DA = NS == 4 ? NS - 1 : NA, DB = NS == 4 ? NS - 1 : NB;
@@ -84,7 +83,7 @@ using Cfg256x256w8 = MacroCfg<256, 256, 64, 2, 4>;  // 8 waves, 128 x 64 per wav
 using Cfg256x128 = MacroCfg<256, 128, 64, 4, 2>;
 using Cfg128x128 = MacroCfg<128, 128, 64, 2, 2>;
 using Cfg64x64 = MacroCfg<64, 64, 64, 2, 2>;
-using Cfg128x128s4 = MacroCfg<128, 128, 64, 2, 2, 4>;  // 4 stages: launches of at most one workgroup per CU
+using Cfg128x128s4 = MacroCfg<128, 128, 64, 2, 4, 4>;  // 4 stages, 8 waves: launches of at most one workgroup per CU
 using Cfg64x64s4 = MacroCfg<64, 64, 64, 2, 2, 4>;
 
 // Physical 16-byte chunk of logical chunk c in a K-contiguous row r (8 chunks per
