@@ -81,7 +81,7 @@ struct MacroCfg {
 
 using Cfg256x256w8 = MacroCfg<256, 256, 64, 2, 4>;  // 8 waves, 128 x 64 per wave
 using Cfg256x128 = MacroCfg<256, 128, 64, 4, 2>;
-using Cfg128x128 = MacroCfg<128, 128, 64, 2, 2>;
+using Cfg128x128 = MacroCfg<128, 128, 64, 2, 4>;      // 8 waves, 64 x 32 per wave
 using Cfg64x64 = MacroCfg<64, 64, 64, 2, 2>;
 using Cfg128x128s4 = MacroCfg<128, 128, 64, 2, 4, 4>;  // 4 stages, 8 waves: launches of at most one workgroup per CU
 using Cfg64x64s4 = MacroCfg<64, 64, 64, 2, 2, 4>;
