@@ -87,12 +87,22 @@ def compare(shapes, seed: int = 0):
     return rows
 
 
-def main(argv=None) -> None:
+def parse_shapes(argv=None):
+    """The shapes a command line asks for (the default list when it names none)."""
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--shape", action="append", default=[], help="M,N,K (repeatable; default: a built-in list)")
     args = ap.parse_args(argv)
-    shapes = [tuple(int(x) for x in s.split(",")) for s in args.shape] or DEFAULT_SHAPES
-    compare(shapes)
+    shapes = []
+    for s in args.shape:
+        dims = tuple(int(x) for x in s.split(","))
+        if len(dims) != 3 or min(dims) < 1:
+            ap.error("--shape takes three positive integers M,N,K, got %r" % s)
+        shapes.append(dims)
+    return shapes or list(DEFAULT_SHAPES)
+
+
+def main(argv=None) -> None:
+    compare(parse_shapes(argv))
 
 
 if __name__ == "__main__":
