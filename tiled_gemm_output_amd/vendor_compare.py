@@ -94,7 +94,10 @@ def parse_shapes(argv=None):
     args = ap.parse_args(argv)
     shapes = []
     for s in args.shape:
-        dims = tuple(int(x) for x in s.split(","))
+        try:
+            dims = tuple(int(x) for x in s.split(","))
+        except ValueError:
+            dims = ()
         if len(dims) != 3 or min(dims) < 1:
             ap.error("--shape takes three positive integers M,N,K, got %r" % s)
         shapes.append(dims)
