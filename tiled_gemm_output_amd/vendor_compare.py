@@ -11,6 +11,7 @@ output is about one rounding of the output).
 
     python -m tiled_gemm_output_amd.vendor_compare                 # the default shape list
     python -m tiled_gemm_output_amd.vendor_compare --shape 4096,4096,4096 --shape 128,8192,8192
+    python -m tiled_gemm_output_amd.vendor_compare --op nt        # B stored N x K (weights), C = A @ B^T
 """
 from __future__ import annotations
 
@@ -44,23 +45,30 @@ def graph_time_us(torch, fn, iters: int) -> float:
     return sorted(times)[1]
 
 
-def compare(shapes, seed: int = 0):
+def compare(shapes, op: str = "nn", seed: int = 0):
+    """op: the stored forms of A and B ("t": A stored K x M, or B stored N x K)."""
     import torch
 
     from . import tgemm
 
     torch.manual_seed(seed)
     h = tgemm.gemm_create()
+    ta, tb = op[0] == "t", op[1] == "t"
     rows = []
     try:
         for M, N, K in shapes:
-            a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
-            b = torch.randn(K, N, device="cuda").to(torch.bfloat16)
+            sa = torch.randn(*((K, M) if ta else (M, K)), device="cuda").to(torch.bfloat16)  # as stored
+            sb = torch.randn(*((N, K) if tb else (K, N)), device="cuda").to(torch.bfloat16)
+            a, b = (sa.t() if ta else sa), (sb.t() if tb else sb)  # the logical M x K and K x N views
             c = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
-            ai, bi, ci = a.view(torch.int16), b.view(torch.int16), c.view(torch.int16)
             flops = 2.0 * M * N * K
             iters = max(3, min(50, int(2e11 / flops)))
-            ours = lambda: tgemm.run_tensors(h, ai, bi, ci, tgemm.BF16_BF16)  # noqa: E731
+
+            def ours():
+                tgemm.check(tgemm.gemm_run_op(h, tgemm.OP_T if ta else tgemm.OP_N, tgemm.OP_T if tb else tgemm.OP_N,
+                                              M, N, K, sa.data_ptr(), sa.stride(0), sb.data_ptr(), sb.stride(0),
+                                              c.data_ptr(), N, tgemm.BF16_BF16, tgemm.current_stream()), "gemm_run_op")
+
             vendor = lambda: torch.matmul(a, b)  # noqa: E731
             for _ in range(3):
                 ours()
@@ -72,9 +80,11 @@ def compare(shapes, seed: int = 0):
             ref = torch.matmul(a.float(), b.float())
             torch.cuda.synchronize()
             err = ((c.float() - ref).abs().max() / ref.abs().max()).item()
-            p = tgemm.gemm_plan(h, M, N, K, a.data_ptr(), K, b.data_ptr(), N, c.data_ptr(), N, tgemm.BF16_BF16)
+            p = tgemm.gemm_plan_op(h, tgemm.OP_T if ta else tgemm.OP_N, tgemm.OP_T if tb else tgemm.OP_N, M, N, K,
+                                   sa.data_ptr(), sa.stride(0), sb.data_ptr(), sb.stride(0), c.data_ptr(), N,
+                                   tgemm.BF16_BF16)
             t = min(t1, t2)
-            rows.append({"shape": (M, N, K), "ours_us": t, "vendor_us": tv, "ours_tflops": flops / t / 1e6,
+            rows.append({"shape": (M, N, K), "op": op, "ours_us": t, "vendor_us": tv, "ours_tflops": flops / t / 1e6,
                          "vendor_tflops": flops / tv / 1e6, "vendor_over_ours": tv / t, "err": err,
                          "plan": "%dx%d, %d K-slices, %d stages%s" % (p["tile_m"], p["tile_n"], p["split_k"], p["stages"],
                                                                      ", tail in %d" % p["tail_split_k"] if p["tail_split_k"] else "")})
@@ -87,10 +97,12 @@ def compare(shapes, seed: int = 0):
     return rows
 
 
-def parse_shapes(argv=None):
-    """The shapes a command line asks for (the default list when it names none)."""
+def parse_args(argv=None):
+    """(shapes, op) of a command line (the default shape list when it names none)."""
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--shape", action="append", default=[], help="M,N,K (repeatable; default: a built-in list)")
+    ap.add_argument("--op", choices=["nn", "nt", "tn", "tt"], default="nn",
+                    help="stored forms: t = that operand is stored transposed (A as K x M, B as N x K)")
     args = ap.parse_args(argv)
     shapes = []
     for s in args.shape:
@@ -101,11 +113,12 @@ def parse_shapes(argv=None):
         if len(dims) != 3 or min(dims) < 1:
             ap.error("--shape takes three positive integers M,N,K, got %r" % s)
         shapes.append(dims)
-    return shapes or list(DEFAULT_SHAPES)
+    return shapes or list(DEFAULT_SHAPES), args.op
 
 
 def main(argv=None) -> None:
-    compare(parse_shapes(argv))
+    shapes, op = parse_args(argv)
+    compare(shapes, op)
 
 
 if __name__ == "__main__":
