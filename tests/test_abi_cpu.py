@@ -193,9 +193,20 @@ def test_plan_split_k():
 def test_plan_stages():
     """The deep pipeline (4 stages of each operand) when the launch has at most one
     workgroup per compute unit (256) and every K-slice has at least 8 K-tiles, except
-    for unsplit 128x128 tiles; the default one (2 A stages, 3 B stages; 3 and 3 for
-    the 64x64 tile) otherwise."""
+    for unsplit 128x128 tiles; 3 A stages and 2 B stages for unsplit 256x256 tiles
+    over a C at most 4 tile columns wide with at least 4 times as many tile rows;
+    the default one (2 A stages, 3 B stages) otherwise."""
     assert plan(8192, 8192, 8192, tgemm.BF16_BF16)["stages"] == 2             # 1024 workgroups
+    assert plan(16384, 1024, 8192, tgemm.BF16_F32)["stages"] == 3             # 64 x 4 tiles
+    assert plan(16384, 1024, 8192, tgemm.BF16_F32, A=0x10001)["stages"] == 2  # odd address: element loader
+    assert plan(12288, 1024, 8192, tgemm.BF16_F32)["stages"] == 3             # 48 x 4 tiles
+    assert plan(16384, 768, 8192, tgemm.BF16_F32)["stages"] == 3              # 64 x 3 tiles
+    p = plan(20480, 1024, 4096, tgemm.BF16_F32)                                # 80 x 4, a split-K tail
+    assert (p["split_k"], p["stages"], p["tail_split_k"]) == (1, 3, 4)
+    assert plan(16384, 1280, 8192, tgemm.BF16_F32)["stages"] == 2             # 64 x 5 tiles
+    assert plan(2048, 16384, 4096, tgemm.BF16_BF16)["stages"] == 2            # 8 x 64 tiles
+    p = plan(1024, 1024, 65536, tgemm.BF16_BF16)                               # 16 tiles of 256x256 x 16 slices
+    assert (p["tile_m"], p["split_k"], p["stages"]) == (256, 16, 2)
     p = plan(128, 8192, 8192, tgemm.BF16_F32)                                  # 64 tiles x 4 slices of 32 K-tiles
     assert (p["grid"] * p["split_k"], p["stages"]) == (256, 4)
     p = plan(768, 768, 8192, tgemm.BF16_BF16)                                  # 36 tiles of 128x128 x 7 slices

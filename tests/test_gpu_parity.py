@@ -482,6 +482,42 @@ def test_deep_pipeline_forced_tile(h, o):
     assert plan_of(h, 520, 264, 2000, tgemm.BF16_F32, tile=(128, 128, 64))["stages"] == 2
 
 
+# ---------------------------------------------------------------- 3 A stages, 2 B stages
+
+ADEEP = [(1100, 250, 6000), (2100, 300, 1096), (3100, 520, 2000), (2065, 257, 777), (1030, 60, 4104),
+         (1300, 200, 4027)]
+
+
+@pytest.mark.parametrize("shape", ADEEP, ids=str)
+def test_a_deep_pipeline(h, o, shape):
+    """The unsplit 256x256 tile over a C at most four tile columns wide and four times
+    as tall loads A three K-steps ahead into three A stages and B two ahead into two
+    (K-tile counts with every remainder of its 6-step stage cycle, ragged K tails, edge
+    tiles): random inputs to the accuracy rule in every format, integer-valued inputs
+    bit for bit in all four operand forms."""
+    M, N, K = shape
+    tile = (256, 256, 64)
+    for n, dtype in enumerate([tgemm.BF16_BF16, tgemm.F16_F32, tgemm.BF16_F32, tgemm.F16_F16]):
+        p = plan_of(h, M, N, K, dtype, tile=tile)
+        assert (p["stages"], p["split_k"]) == (3, 1), p
+        a, b = inputs.random_case(M, N, K, G.IN_KIND[dtype], seed=K + 7 * n)
+        check_full(h, o, a, b, dtype, tile=tile)
+    for kind, dtype in [("bf16", tgemm.BF16_F32), ("f16", tgemm.F16_F16)]:
+        a = inputs.draw((M, K), "small_int", kind, 81)
+        b = inputs.draw((K, N), "small_int", kind, 83)
+        ref = oracle_ref(o, a, b, dtype).view(G.np_int(tgemm.OUT_BYTES[dtype]))
+        set_tile(h, tile)
+        try:
+            for ops in [(tgemm.OP_N, tgemm.OP_N), (tgemm.OP_N, tgemm.OP_T), (tgemm.OP_T, tgemm.OP_N),
+                        (tgemm.OP_T, tgemm.OP_T)]:
+                print("a-deep %s %s ops %s" % (shape, kind, ops), flush=True)
+                c, dc = G.run(h, a, b, dtype, op_a=ops[0], op_b=ops[1])
+                assert dc.untouched_outside()
+                assert np.array_equal(c, ref), ops
+        finally:
+            set_tile(h, None)
+
+
 # ---------------------------------------------------------------- output rounding edge cases
 
 def test_output_rounding_edge_values(h, o):
@@ -631,15 +667,18 @@ def test_odd_byte_addresses(h, o, shape, dtype):
     G.compare(c, ref, G.OUT_KIND[dtype])
 
 
-@pytest.mark.parametrize("tile", [(64, 64, 64), (128, 128, 64), (256, 128, 64), (256, 256, 64)], ids=str)
-def test_k_step_counts(h, o, tile):
+@pytest.mark.parametrize("tile,tall", [((64, 64, 64), False), ((128, 128, 64), False), ((256, 128, 64), False),
+                                       ((256, 256, 64), False), ((256, 256, 64), True)], ids=str)
+def test_k_step_counts(h, o, tile, tall):
     """Stage bookkeeping at the smallest K-step counts: 1 to 13 K-tiles (every remainder
-    of the 6-step and 3-step stage cycles, before and after one or two whole cycles;
-    full, and with a partial last K-tile), 2 x 2 ragged tiles, integer-valued inputs
-    (exact in any order): every run matches the oracle bit for bit and a second run
-    repeats it."""
+    of the 6-step stage cycles, before and after one or two whole cycles; full, and with
+    a partial last K-tile), 2 x 2 ragged tiles, or 9 x 2 (tall: the 256x256 tile with
+    three A stages and two B stages), integer-valued inputs (exact in any order): every
+    run matches the oracle bit for bit and a second run repeats it."""
     tm, tn, tk = tile
-    M, N = tm + 17, tn + 5
+    M, N = (8 * tm + 17, tn + 5) if tall else (tm + 17, tn + 5)
+    if tile == (256, 256, 64):
+        assert plan_of(h, M, N, 13 * tk, tgemm.BF16_F32, tile=tile)["stages"] == (3 if tall else 2)
     for nk in range(1, 14):
         for K in (tk * nk, tk * nk - 13):
             a = inputs.draw((M, K), "small_int", "bf16", 100 + K)

@@ -11,7 +11,8 @@ from tiled_gemm_output_amd import tgemm
 CHOICES = [
     ((8192, 8192, 8192), (256, 256, 1, 2, 0)),       # the 256x256 tile from one full round on
     ((4096, 4096, 4096), (256, 256, 1, 2, 0)),
-    ((16384, 1024, 8192), (256, 256, 1, 2, 0)),
+    ((16384, 1024, 8192), (256, 256, 1, 3, 0)),      # 4 tile columns: A three K-steps ahead, 203.8 (211.6)
+    ((1024, 16384, 8192), (256, 256, 1, 2, 0)),      # 211.8 (224.0 with A three ahead)
     ((6000, 6000, 6000), (256, 256, 1, 2, 3)),       # partly full last round as a split-K tail
     ((128, 8192, 8192), (128, 128, 4, 4, 0)),        # HBM-bound: 4 slices, one per CU, 4 stages (34.7 vs 39.8 with 8)
     ((2048, 1024, 8192), (128, 128, 4, 2, 0)),       # 128 tiles: 44.6 (was 71.7 unsplit)
@@ -22,9 +23,9 @@ CHOICES = [
     ((6713, 307, 3517), (128, 128, 3, 2, 0)),        # 43.3 (49.8 unsplit)
     ((768, 768, 8192), (128, 128, 7, 4, 0)),         # 24.0 (44.8 as 144 unsplit 64x64 tiles)
     ((768, 768, 2048), (64, 64, 1, 4, 0)),           # 13.5 (17.1 as 128x128 split)
-    ((3072, 1536, 8192), (256, 256, 3, 2, 0)),       # 84.5 (102.7 as 128x128)
+    ((3072, 1536, 8192), (256, 256, 3, 2, 0)),       # 84.5 (102.7 as 128x128; 92.4 against 89.7 with A three ahead)
     ((8954, 586, 5871), (256, 256, 2, 2, 0)),        # 97.1 (108.9 as 128x128)
-    ((1024, 1024, 65536), (256, 256, 16, 2, 0)),     # 154.4 (172.7 as 128x128 in 4)
+    ((1024, 1024, 65536), (256, 256, 16, 2, 0)),     # 154.4 (172.7 as 128x128 in 4; 151 against 140 with A three ahead)
     ((512, 2048, 8192), (128, 128, 4, 4, 0)),        # 32.1 (33.5 with 8 slices, two per CU)
     ((1024, 1024, 1024), (64, 64, 1, 4, 0)),         # short K: 64x64
     ((257, 2440, 3976), (128, 128, 4, 4, 0)),        # 60 tiles: 20.4 (27.2 as 195 unsplit 64x64 tiles)

@@ -28,7 +28,7 @@ struct MacroArgs {
 struct MacroShape {
   int bm, bn, bk, threads, lds, stages;
 };
-constexpr int kNumMacroShapes = 6;
+constexpr int kNumMacroShapes = 7;
 extern const MacroShape kMacroShapes[kNumMacroShapes];
 
 // in: 0 = f16, 1 = bf16. out: 0 = f32, 1 = bf16, 2 = f16. ta: A is stored transposed

@@ -170,6 +170,7 @@ const MacroShape kMacroShapes[kNumMacroShapes] = {
     {64, 64, 64, Cfg64x64::kThreads, Cfg64x64::kLds, Cfg64x64::NS},
     {128, 128, 64, Cfg128x128s4::kThreads, Cfg128x128s4::kLds, Cfg128x128s4::NS},
     {64, 64, 64, Cfg64x64s4::kThreads, Cfg64x64s4::kLds, Cfg64x64s4::NS},
+    {256, 256, 64, Cfg256x256w8a::kThreads, Cfg256x256w8a::kLds, Cfg256x256w8a::NS},
 };
 
 // The launchers live in macro_tile_inst_*.hip.

@@ -1,0 +1,9 @@
+// macro_tile_inst_nt_big3.hip -- macro-tile GEMM kernels for C = A @ B^T (B supplied as N x K), the 256x256 tile
+// with A loaded three K-steps ahead.
+#include "macro_tile_kernel.h"
+
+namespace tg {
+
+template hipError_t launch_dtype<Cfg256x256w8a, false, true>(const MacroArgs&, int, int, bool, hipStream_t, int64_t, int);
+
+}  // namespace tg

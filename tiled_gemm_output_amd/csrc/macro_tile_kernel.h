@@ -20,10 +20,11 @@
 //    v_mfma_f32_32x32x16_{bf16,f16};
 //  * a pipeline of LDS stages with one barrier per K-step: K-tile kt lives in A
 //    stage kt % NA and B stage kt % NB; A is loaded DA and B DB steps before the
-//    step that multiplies it (by default two A stages and three B stages, DA = 2 and
-//    DB = 3; four of each and DA = DB = 3 for launches with at most one workgroup
-//    per compute unit). A stage is only ever refilled once every wave's reads of it
-//    have completed (see the main loop);
+//    step that multiplies it (two A stages and three B stages, DA = 2 and DB = 3;
+//    three A stages and two B stages, DA = 3 and DB = 2; or four of each and
+//    DA = DB = 3 for launches with at most one workgroup per compute unit). A stage is
+//    only ever refilled once every wave's reads of it have completed (see the main
+//    loop);
 //  * vector path (A and B at even addresses: any shape and leading dimension):
 //    16-byte buffer loads straight from global memory into LDS (buffer_load_dwordx4
 //    ... lds), no register staging; out-of-range lanes use an offset beyond the
@@ -49,7 +50,9 @@ namespace tg {
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
 // NS names the pipeline: 2 = two A stages, A loaded two steps ahead, and three B
-// stages, B loaded three steps ahead; 4 = four stages of each, loaded three steps ahead.
+// stages, B loaded three steps ahead; 3 = three A stages, A loaded three steps ahead,
+// and two B stages, B loaded two steps ahead; 4 = four stages of each, loaded three
+// steps ahead.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int NS_ = 2>
 struct MacroCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, NS = NS_;
@@ -60,14 +63,14 @@ struct MacroCfg {
   static constexpr int kABytes = BM * BK * 2, kBBytes = BK * BN * 2;
   static constexpr int kSubsteps = BK / 16;
   static constexpr int NA = NS == 2 ? 2 : NS;  // A stages
-  static constexpr int NB = NS == 2 ? 3 : NS;  // B stages
+  static constexpr int NB = NS == 2 ? 3 : (NS == 3 ? 2 : NS);  // B stages
   // K-steps between a K-tile's load (issued right after one step's barrier) and the
   // step that multiplies it: every stage not holding a K-tile still to be multiplied.
   static constexpr int DA = NS == 4 ? NS - 1 : NA, DB = NS == 4 ? NS - 1 : NB;
   static constexpr int L = NA / gcd_c(NA, NB) * NB;  // steps after which the stage pattern repeats
   static constexpr int kLds = NA * kABytes + NB * kBBytes;
   static_assert(BK == 64, "four 16-deep substeps per K-step");
-  static_assert(NS == 2 || NS == 4, "two pipelines");
+  static_assert(NS == 2 || NS == 3 || NS == 4, "three pipelines");
   // Every wave has completed its LDS reads of K-tile st when it reaches step st's
   // barrier, so the refill of K-tile st + DA (st + DB), issued right after it, may
   // take the stage of st but none of st + 1 .. st + DA - 1 (DB - 1): NA >= DA, NB >= DB.
@@ -80,6 +83,7 @@ struct MacroCfg {
 };
 
 using Cfg256x256w8 = MacroCfg<256, 256, 64, 2, 4>;  // 8 waves, 128 x 64 per wave
+using Cfg256x256w8a = MacroCfg<256, 256, 64, 2, 4, 3>;  // the same, A loaded three K-steps ahead
 using Cfg256x128 = MacroCfg<256, 128, 64, 4, 2>;
 using Cfg128x128 = MacroCfg<128, 128, 64, 2, 4>;      // 8 waves, 64 x 32 per wave
 using Cfg64x64 = MacroCfg<64, 64, 64, 2, 2>;
@@ -786,7 +790,8 @@ hipError_t launch_dtype(const MacroArgs& a, int in, int out, bool vec, hipStream
 
 // The tile configurations, in the order of kMacroShapes (the shape index of launch_macro):
 // X(index, configuration).
-#define TG_MACRO_CONFIGS(X) \
-  X(0, Cfg256x256w8) X(1, Cfg256x128) X(2, Cfg128x128) X(3, Cfg64x64) X(4, Cfg128x128s4) X(5, Cfg64x64s4)
+#define TG_MACRO_CONFIGS(X)                                                                           \
+  X(0, Cfg256x256w8) X(1, Cfg256x128) X(2, Cfg128x128) X(3, Cfg64x64) X(4, Cfg128x128s4) X(5, Cfg64x64s4) \
+  X(6, Cfg256x256w8a)
 
 }  // namespace tg
