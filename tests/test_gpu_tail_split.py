@@ -106,6 +106,48 @@ def test_tail_split_large_sampled(h, o, shape):
     G.compare(got_c, o.gemm_cols(a, b, cols, "bf16", "bf16").view(np.int16), "bf16")
 
 
+def test_tail_split_tall_a_deep(h, o):
+    """A tall, narrow product whose full rounds and split-K tail both run the 256x256
+    tile with A loaded three K-steps ahead: integer-valued inputs exact on sampled rows
+    (every tail row among them) and columns; float inputs give the rows before the
+    tail bit for bit as a forced-tile run (one launch, no tail)."""
+    import torch
+
+    M, N, K = 17408, 1024, 2048
+    p = tail_plan(h, M, N, K, (N_, N_), tgemm.BF16_F32)
+    m0 = p["tail_m0"]
+    assert (p["stages"], p["tail_split_k"] > 1, m0) == (3, True, 16384), p
+    rows, cols = inputs.sample_rows_cols(M, N, seed=11, block=256)
+    rows = np.unique(np.concatenate([rows, np.arange(m0, M, 97, dtype=rows.dtype), [M - 1]]))
+
+    def run(a, b):
+        da = torch.from_numpy(a.view(np.int16)).cuda()
+        db = torch.from_numpy(b.view(np.int16)).cuda()
+        dc = torch.full((M, N), G.SENTINEL[4], dtype=torch.int32, device="cuda")
+        tgemm.check(tgemm.gemm_run(h, M, N, K, da.data_ptr(), K, db.data_ptr(), N, dc.data_ptr(), N,
+                                   tgemm.BF16_F32, torch.cuda.current_stream().cuda_stream), "gemm_run")
+        torch.cuda.synchronize()
+        return dc
+
+    a = inputs.draw((M, K), "small_int", "bf16", 91)
+    b = inputs.draw((K, N), "small_int", "bf16", 92)
+    print("tall a-deep tail: tail_m0 %d S %d, integer inputs" % (m0, p["tail_split_k"]), flush=True)
+    dc = run(a, b)
+    assert np.array_equal(dc[torch.from_numpy(rows).cuda()].cpu().numpy(), o.gemm_rows(a, b, rows, "bf16", "f32").view(np.int32))
+    assert np.array_equal(dc[:, torch.from_numpy(cols).cuda()].cpu().numpy(), o.gemm_cols(a, b, cols, "bf16", "f32").view(np.int32))
+    a, b = inputs.random_case(M, N, K, "bf16", seed=93)
+    c = run(a, b).cpu().numpy()
+    G.compare(c[rows], o.gemm_rows(a, b, rows, "bf16", "f32").view(np.int32), "f32")
+    tgemm.check(tgemm.gemm_set_tile(h, 256, 256, 64), "gemm_set_tile")
+    try:
+        q = tail_plan(h, M, N, K, (N_, N_), tgemm.BF16_F32)
+        assert (q["tail_split_k"], q["stages"]) == (0, 3), q  # forced tile: no tail, same pipeline
+        c_plain = run(a, b).cpu().numpy()
+    finally:
+        tgemm.gemm_set_tile(h, 0, 0, 0)
+    assert np.array_equal(c[:m0], c_plain[:m0])
+
+
 def tail_cases():
     """Tile counts of one or two full rounds plus a few tiles (ragged last tiles),
     random K, leading-dimension padding and operand forms."""

@@ -72,6 +72,23 @@ def test_two_calls_in_a_row_match_gemm_run_op(o):
         tgemm.gemm_destroy(h)
 
 
+def test_tall_product_a_three_steps_ahead(o):
+    """A tall, narrow product (the 256x256 tile with A loaded three K-steps ahead,
+    ragged K): bit-identical to gemm_run_op, and the oracle's result on sampled rows."""
+    h = tgemm.gemm_create()
+    try:
+        M, N, K, dtype = 16384, 1024, 200, tgemm.BF16_BF16
+        p = tgemm.gemm_plan(h, M, N, K, 1 << 20, K, 1 << 30, N, 1 << 34, N, dtype)
+        assert (p["tile_m"], p["split_k"], p["stages"]) == (256, 1, 3), p
+        a, b = inputs.random_case(M, N, K, "bf16", seed=7)
+        ref, new = both(h, M, N, K, dev16(a), dev16(b), dtype)
+        assert np.array_equal(new, ref)
+        rows, _ = inputs.sample_rows_cols(M, N, seed=7, block=256)
+        G.compare(new[rows], o.gemm_rows(a, b, rows, "bf16", "bf16").view(np.int16), "bf16")
+    finally:
+        tgemm.gemm_destroy(h)
+
+
 def test_split_k_tail_and_operand_copies(o):
     """A plan with a split-K tail whose partial tiles fit (run as gemm_run_op runs it)
     and a plan that copies A into aligned rows (not done here: the kernels read the
