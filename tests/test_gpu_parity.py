@@ -518,6 +518,39 @@ def test_a_deep_pipeline(h, o, shape):
             set_tile(h, None)
 
 
+def a_deep_cases():
+    """Random tall, narrow products that take three A stages on the forced 256x256 tile
+    (at most 4 tile columns, at least 4 times as many tile rows): ragged M, N and K,
+    leading-dimension padding, C offsets, every operand form and format."""
+    rng = np.random.default_rng(777)
+    dtypes = [tgemm.BF16_F32, tgemm.BF16_BF16, tgemm.F16_F32, tgemm.F16_F16]
+    ops = [(tgemm.OP_N, tgemm.OP_N), (tgemm.OP_T, tgemm.OP_N), (tgemm.OP_N, tgemm.OP_T), (tgemm.OP_T, tgemm.OP_T)]
+    cases = []
+    for n in range(12):
+        tn = int(rng.integers(1, 3))
+        tm = 4 * tn + int(rng.integers(0, 2))
+        M = 256 * (tm - 1) + int(rng.integers(1, 257))
+        N = 256 * (tn - 1) + int(rng.integers(1, 257))
+        K = int(rng.integers(65, 1500))
+        pad = [0, 1, 8, 37][n % 4]
+        coff = int(rng.integers(0, 9)) if n % 3 else 0
+        cases.append((M, N, K, dtypes[n % 4], pad, coff, ops[(n // 2) % 4]))
+    return cases
+
+
+@pytest.mark.parametrize("case", a_deep_cases(), ids=str)
+def test_a_deep_random(h, o, case):
+    M, N, K, dtype, pad, coff, op = case
+    p = plan_of(h, M, N, K, dtype, tile=(256, 256, 64))
+    assert p["stages"] == 3, (case, p)
+    a, b = inputs.random_case(M, N, K, G.IN_KIND[dtype], seed=M + 3 * N + 7 * K)
+    lda = (M if op[0] == tgemm.OP_T else K) + pad
+    ldb = (K if op[1] == tgemm.OP_T else N) + pad
+    print("a-deep random %s" % (case,), flush=True)
+    check_full(h, o, a, b, dtype, tile=(256, 256, 64), lda=lda, ldb=ldb, ldc=N + pad, offs=(0, 0, coff),
+               op_a=op[0], op_b=op[1])
+
+
 # ---------------------------------------------------------------- output rounding edge cases
 
 def test_output_rounding_edge_values(h, o):
