@@ -101,12 +101,12 @@ typedef struct {
   int32_t stages;                 /* the macro-tile kernel's LDS pipeline: 2 (A loaded two K-steps ahead
                                      into two A stages, B three ahead into three B stages); 3 (A loaded
                                      three K-steps ahead into three A stages, B two ahead into two B
-                                     stages) for the 256x256 tile, unsplit, when C has at most four tile
-                                     columns and at least four times as many tile rows; or 4 (both loaded three K-steps ahead
-                                     into four stages of each) when the launch has at most one workgroup
-                                     per compute unit and its tiles are 64x64 or cut into K-slices; 2 for
-                                     the 16x16x32 tile (two stages of each), 1 for the int32 kernel, 0
-                                     when nothing is launched */
+                                     stages) for the 256x256 tile when C has at most four tile columns
+                                     and at least four times as many tile rows; or 4 (both loaded three
+                                     K-steps ahead into four stages of each) when the launch has at most
+                                     one workgroup per compute unit and its tiles are 64x64 or cut into
+                                     K-slices; 2 for the 16x16x32 tile (two stages of each), 1 for the
+                                     int32 kernel, 0 when nothing is launched */
   int32_t tail_split_k;           /* 0, or S > 1: the tiles of C rows [tail_m0, M) run after the others
                                      as a second launch of the same tile with S K-slices (fp32 partial
                                      tiles summed in slice order), so that they fill the compute units

@@ -193,9 +193,9 @@ def test_plan_split_k():
 def test_plan_stages():
     """The deep pipeline (4 stages of each operand) when the launch has at most one
     workgroup per compute unit (256) and every K-slice has at least 8 K-tiles, except
-    for unsplit 128x128 tiles; 3 A stages and 2 B stages for unsplit 256x256 tiles
-    over a C at most 4 tile columns wide with at least 4 times as many tile rows;
-    the default one (2 A stages, 3 B stages) otherwise."""
+    for unsplit 128x128 tiles; 3 A stages and 2 B stages for 256x256 tiles over a C
+    at most 4 tile columns wide with at least 4 times as many tile rows (split or
+    not); the default one (2 A stages, 3 B stages) otherwise."""
     assert plan(8192, 8192, 8192, tgemm.BF16_BF16)["stages"] == 2             # 1024 workgroups
     assert plan(16384, 1024, 8192, tgemm.BF16_F32)["stages"] == 3             # 64 x 4 tiles
     assert plan(16384, 1024, 8192, tgemm.BF16_F32, A=0x10001)["stages"] == 2  # odd address: element loader
@@ -207,6 +207,8 @@ def test_plan_stages():
     assert plan(2048, 16384, 4096, tgemm.BF16_BF16)["stages"] == 2            # 8 x 64 tiles
     p = plan(1024, 1024, 65536, tgemm.BF16_BF16)                               # 16 tiles of 256x256 x 16 slices
     assert (p["tile_m"], p["split_k"], p["stages"]) == (256, 16, 2)
+    p = plan(16384, 512, 8192, tgemm.BF16_BF16)                                # 64 x 2 tiles x 2 slices
+    assert (p["tile_m"], p["split_k"], p["stages"]) == (256, 2, 3)
     p = plan(128, 8192, 8192, tgemm.BF16_F32)                                  # 64 tiles x 4 slices of 32 K-tiles
     assert (p["grid"] * p["split_k"], p["stages"]) == (256, 4)
     p = plan(768, 768, 8192, tgemm.BF16_BF16)                                  # 36 tiles of 128x128 x 7 slices

@@ -518,6 +518,34 @@ def test_a_deep_pipeline(h, o, shape):
             set_tile(h, None)
 
 
+@pytest.mark.parametrize("shape,splits", [((2100, 300, 6000), 3), ((1300, 200, 4027), 2), ((3100, 520, 2000), 5)],
+                         ids=str)
+def test_a_deep_split_k(h, o, shape, splits):
+    """Three A stages in K-slices (a forced 256x256 tile over a tall, narrow C, forced
+    slice counts, ragged K): integer-valued inputs bit for bit in two operand forms,
+    random inputs to the accuracy rule."""
+    M, N, K = shape
+    tile = (256, 256, 64)
+    p = plan_of(h, M, N, K, tgemm.BF16_F32, splits=splits, tile=tile)
+    assert (p["stages"], p["split_k"]) == (3, splits), p
+    a = inputs.draw((M, K), "small_int", "bf16", 61)
+    b = inputs.draw((K, N), "small_int", "bf16", 62)
+    ref = oracle_ref(o, a, b, tgemm.BF16_F32).view(np.int32)
+    set_tile(h, tile)
+    tgemm.check(tgemm.gemm_set_split_k(h, splits), "gemm_set_split_k")
+    try:
+        for ops in [(tgemm.OP_N, tgemm.OP_N), (tgemm.OP_T, tgemm.OP_T)]:
+            print("a-deep split %s S %d ops %s" % (shape, splits, ops), flush=True)
+            c, dc = G.run(h, a, b, tgemm.BF16_F32, op_a=ops[0], op_b=ops[1])
+            assert dc.untouched_outside()
+            assert np.array_equal(c, ref), ops
+    finally:
+        set_tile(h, None)
+        tgemm.gemm_set_split_k(h, 0)
+    a, b = inputs.random_case(M, N, K, "bf16", seed=K + splits)
+    check_full(h, o, a, b, tgemm.BF16_BF16, tile=tile, splits=splits)
+
+
 def a_deep_cases():
     """Random tall, narrow products that take three A stages on the forced 256x256 tile
     (at most 4 tile columns, at least 4 times as many tile rows): ragged M, N and K,

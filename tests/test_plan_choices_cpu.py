@@ -24,7 +24,8 @@ CHOICES = [
     ((768, 768, 8192), (128, 128, 7, 4, 0)),         # 24.0 (44.8 as 144 unsplit 64x64 tiles)
     ((768, 768, 2048), (64, 64, 1, 4, 0)),           # 13.5 (17.1 as 128x128 split)
     ((3072, 1536, 8192), (256, 256, 3, 2, 0)),       # 84.5 (102.7 as 128x128; 92.4 against 89.7 with A three ahead)
-    ((8954, 586, 5871), (256, 256, 2, 2, 0)),        # 97.1 (108.9 as 128x128)
+    ((8954, 586, 5871), (256, 256, 2, 3, 0)),        # 97.1 (108.9 as 128x128); 35 x 3 tiles: A three K-steps ahead
+    ((16384, 512, 8192), (256, 256, 2, 3, 0)),       # 64 x 2 tiles in 2 slices: 131.1-132.4 (137.4-139.2 with A two ahead)
     ((1024, 1024, 65536), (256, 256, 16, 2, 0)),     # 154.4 (172.7 as 128x128 in 4; 151 against 140 with A three ahead)
     ((512, 2048, 8192), (128, 128, 4, 4, 0)),        # 32.1 (33.5 with 8 slices, two per CU)
     ((1024, 1024, 1024), (64, 64, 1, 4, 0)),         # short K: 64x64

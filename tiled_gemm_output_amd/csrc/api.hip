@@ -558,22 +558,24 @@ gemm_status_t plan_impl(const tgemm_handle* h, int op_a, int op_b, int64_t M, in
         p.lds_bytes = tg::kMacroShapes[deep].lds;
       }
     }
-    // An unsplit 256x256 tile over a C at most four tile columns wide and at least four
-    // times as many tile rows loads A three K-steps ahead into three A stages and B two
-    // ahead into two B stages: each A panel serves at most four tiles, and A's loads are
-    // the ones that miss the cache (MI355X, bf16, same process, alternating batches of
-    // about 100 launches at the clock the power limit holds, bit-identical results:
-    // 16384x1024x8192 203.8 against 211.6 us, with A stored K x M 197.3 against 206.3).
-    // Elsewhere A stays two steps ahead: the two measure within 1% on wider products
-    // (8192^3 813 against 810, 16384x2048x4096 205.3 against 205.6, 6144x8192x8192 585
-    // against 582), and A three ahead is slower on wide ones (1024x16384x8192 224.0
-    // against 211.8), on 3072x3072x8192 (144.8 against 141.5), in K-slices
-    // (1024x1024x65536 in 16 slices 151 against 140) and on the smaller tiles
-    // (2560x2560x4096 on 256x128 58.0 against 52.7). A split-K tail after the full rounds
-    // runs with the same pipeline as the rounds.
+    // A 256x256 tile over a C at most four tile columns wide and at least four times as
+    // many tile rows loads A three K-steps ahead into three A stages and B two ahead into
+    // two B stages: each A panel serves at most four tiles, and A's loads are the ones
+    // that miss the cache (MI355X, bf16, same process, alternating batches of about 100
+    // launches at the clock the power limit holds, bit-identical results:
+    // 16384x1024x8192 203.8 against 211.6 us, with A stored K x M 197.3 against 206.3,
+    // 16384x768x8192 171.1 against 190.4; plans in 2 K-slices, bench.py in alternating
+    // processes: 16384x512x8192 131.1-132.4 against 137.4-139.2, 8954x586x5871 94.5-95.4
+    // against 95.9-96.5, within 1% on 12288x512x8192 and 8192x1024x8192). Elsewhere A stays two steps ahead: the two
+    // measure within 1% on wider products (8192^3 813 against 810, 16384x2048x4096 205.3
+    // against 205.6, 6144x8192x8192 585 against 582), and A three ahead is slower on wide
+    // ones (1024x16384x8192 224.0 against 211.8), on 3072x3072x8192 (144.8 against
+    // 141.5), on square-ish products in K-slices (1024x1024x65536 in 16 slices 151 against
+    // 140) and on the smaller tiles (2560x2560x4096 on 256x128 58.0 against 52.7). A
+    // split-K tail after the full rounds runs with the same pipeline as the rounds.
     const int64_t tiles_m = cdiv(M, p.tile_m), tiles_n = cdiv(N, p.tile_n);
-    if (p.kernel == 4 && p.vector_loads && p.stages == 2 && p.split_k == 1 && p.tile_m == 256 &&
-        p.tile_n == 256 && tiles_n <= 4 && tiles_m >= 4 * tiles_n) {
+    if (p.kernel == 4 && p.vector_loads && p.stages == 2 && p.tile_m == 256 && p.tile_n == 256 && tiles_n <= 4 &&
+        tiles_m >= 4 * tiles_n) {
       const int adeep = find_macro(p.tile_m, p.tile_n, p.tile_k, 3);
       if (adeep >= 0) {
         p.stages = 3;
@@ -942,8 +944,8 @@ gemm_status_t gemm_tune(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t
     const bool vec = base.vector_loads != 0;
 
     // Candidates: the automatic plan when it has a split-K tail, every 2-stage macro
-    // tile with K-slice counts up to 32 (each slice at least 2 K-tiles), the 3-stage
-    // twin unsplit and the 4-stage twins where they apply, and the one-wave 16x16x32 tile for small outputs. Where
+    // tile with K-slice counts up to 32 (each slice at least 2 K-tiles), the 3- and
+    // 4-stage twins where they apply, and the one-wave 16x16x32 tile for small outputs. Where
     // an operand's rows are off cache lines (and the handle does not force the choice),
     // each macro-tile candidate is tried with every subset of those operands copied
     // into aligned rows that keeps the direct loads.
@@ -983,7 +985,7 @@ gemm_status_t gemm_tune(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_b, int64_t
         if (sk > 1 && (nk / sk < 2 || grid * sk > kTuneMaxWorkgroups)) continue;
         const int eff = sk > 1 ? (int)cdiv(nk, cdiv(nk, sk)) : 1;
         add(tune_choice{4, m.bm, m.bn, m.bk, eff, 2});
-        if (vec && eff == 1 && find_macro(m.bm, m.bn, m.bk, 3) >= 0) add(tune_choice{4, m.bm, m.bn, m.bk, 1, 3});
+        if (vec && find_macro(m.bm, m.bn, m.bk, 3) >= 0) add(tune_choice{4, m.bm, m.bn, m.bk, eff, 3});
         if (vec && find_macro(m.bm, m.bn, m.bk, 4) >= 0 && cdiv(nk, eff) >= 4) add(tune_choice{4, m.bm, m.bn, m.bk, eff, 4});
       }
     }
