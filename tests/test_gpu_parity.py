@@ -579,6 +579,62 @@ def test_a_deep_random(h, o, case):
                op_a=op[0], op_b=op[1])
 
 
+# Two seeded shapes per branch of the automatic plan (tile, K-slices or not, pipeline, split-K
+# tail), drawn from M in [100, 17000), N in [100, 9000), K in [64, 12000); the plan each one
+# takes is pinned, so that a planner change that moves one shows up here.
+AUTO_BRANCHES = [
+    ((4630, 326, 1943), (64, 64, False, 2, False)),
+    ((3076, 360, 327), (64, 64, False, 2, False)),
+    ((2987, 139, 2570), (64, 64, False, 4, False)),
+    ((240, 2586, 2652), (64, 64, False, 4, False)),
+    ((3278, 121, 6258), (64, 64, True, 4, False)),
+    ((465, 484, 4438), (64, 64, True, 4, False)),
+    ((592, 6188, 3428), (128, 128, False, 2, False)),
+    ((609, 5890, 6252), (128, 128, False, 2, False)),
+    ((1852, 1230, 7266), (128, 128, True, 2, False)),
+    ((1715, 633, 10028), (128, 128, True, 2, False)),
+    ((143, 2665, 5655), (128, 128, True, 4, False)),
+    ((218, 3498, 5076), (128, 128, True, 4, False)),
+    ((1337, 4370, 3563), (256, 128, False, 2, False)),
+    ((7032, 558, 3016), (256, 128, False, 2, False)),
+    ((10719, 3285, 488), (256, 256, False, 2, False)),
+    ((14474, 5504, 827), (256, 256, False, 2, False)),
+    ((9429, 3744, 2837), (256, 256, False, 2, True)),
+    ((3207, 5928, 6132), (256, 256, False, 2, True)),
+    ((16426, 726, 9337), (256, 256, False, 3, False)),
+    ((10947, 876, 304), (256, 256, False, 3, False)),
+    ((1372, 3793, 10997), (256, 256, True, 2, False)),
+    ((1542, 4169, 6705), (256, 256, True, 2, False)),
+    ((10298, 522, 8356), (256, 256, True, 3, False)),
+    ((11573, 492, 6177), (256, 256, True, 3, False)),
+]
+
+
+@pytest.mark.parametrize("shape,branch", AUTO_BRANCHES, ids=str)
+def test_automatic_plan_branches(h, o, shape, branch):
+    """Every branch of the automatic plan on ragged shapes of medium to large size (dense
+    row-major operands, bf16 in and out): sampled rows and columns (one per 256, the
+    first and the last) against the oracle."""
+    import torch
+
+    M, N, K = shape
+    p = plan_of(h, M, N, K, tgemm.BF16_BF16)
+    got = (p["tile_m"], p["tile_n"], p["split_k"] > 1, p["stages"], p["tail_split_k"] > 0)
+    assert got == branch, (shape, p)
+    a, b = inputs.random_case(M, N, K, "bf16", seed=M + N + K)
+    print("plan branch %s %s" % (shape, branch), flush=True)
+    da = torch.from_numpy(a.view(np.int16)).cuda()
+    db = torch.from_numpy(b.view(np.int16)).cuda()
+    dc = torch.full((M, N), G.SENTINEL[2], dtype=torch.int16, device="cuda")
+    tgemm.check(tgemm.gemm_run(h, M, N, K, da.data_ptr(), K, db.data_ptr(), N, dc.data_ptr(), N, tgemm.BF16_BF16,
+                               torch.cuda.current_stream().cuda_stream), "gemm_run")
+    torch.cuda.synchronize()
+    rows, cols = inputs.sample_rows_cols(M, N, seed=M, block=256)
+    G.compare(dc[torch.from_numpy(rows).cuda()].cpu().numpy(), o.gemm_rows(a, b, rows, "bf16", "bf16").view(np.int16), "bf16")
+    G.compare(dc[:, torch.from_numpy(cols).cuda()].cpu().numpy(), o.gemm_cols(a, b, cols, "bf16", "bf16").view(np.int16),
+              "bf16")
+
+
 # ---------------------------------------------------------------- output rounding edge cases
 
 def test_output_rounding_edge_values(h, o):
