@@ -219,7 +219,8 @@ gemm_status_t gemm_run_op_noalloc(gemm_handle_t h, gemm_op_t op_a, gemm_op_t op_
 /* Choose the fastest plan for one call's shape by measurement (the pages' Helion
  * page: the compiler tunes the tile size automatically). Runs every candidate --
  * each macro tile (256x256, 256x128, 128x128, 64x64) with K-slice counts up to 32,
- * the 4-stage twins where they apply, and the 16x16x32 tile for outputs of up to
+ * the 256x256 tile also with A loaded three K-steps ahead (stages 3), the 4-stage
+ * twins where they apply, and the 16x16x32 tile for outputs of up to
  * 2^20 elements; where an operand's rows are off 128-byte boundaries and the handle
  * leaves operand copies automatic (gemm_set_repack 0), each macro-tile candidate
  * also with every subset of those operands copied into aligned rows -- on the
